@@ -1,0 +1,152 @@
+"""ctypes front end of the fp64 CPU oracle for conv2d dgrad.
+
+TEST INFRASTRUCTURE: only tests/, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package. The product package
+``convolution_backward_amd`` never imports it and shares no code with it.
+
+The arithmetic lives in ``dgrad_oracle.c`` (plain C, built with gcc and
+OpenMP); this file only builds/loads it and marshals numpy arrays.
+Functions whose results have no independent pin are listed in the C file's
+header; at present every function here is pinned by ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "dgrad_oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+EPI_NONE, EPI_DRELU, EPI_DHARDSWISH = 0, 1, 2
+
+# Portable ISA level: the library is built here and may run on another host.
+CFLAGS = ["-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
+
+
+def build(src: str = SRC, out: str = LIB, extra=()) -> str:
+    """Compile the oracle with gcc. Always recompiles."""
+    cmd = ["gcc", *CFLAGS, *extra, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_lib = None
+
+
+def _bind(lib):
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    i = ctypes.c_int
+    lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_half_to_double.restype = ctypes.c_double
+    lib.oracle_double_to_half_rne.argtypes = [ctypes.c_double]
+    lib.oracle_double_to_half_rne.restype = ctypes.c_uint16
+    lib.oracle_relu_grad.argtypes = [ctypes.c_double]
+    lib.oracle_relu_grad.restype = ctypes.c_double
+    lib.oracle_hardswish_grad.argtypes = [ctypes.c_double]
+    lib.oracle_hardswish_grad.restype = ctypes.c_double
+    lib.oracle_out_extent.argtypes = [i, i, i, i]
+    lib.oracle_out_extent.restype = i
+    lib.oracle_dgrad_rows.argtypes = [u16p, u16p, u16p] + [i] * 10 + [i64p, ctypes.c_int64, f64p, i]
+    lib.oracle_dgrad_rows.restype = i
+    lib.oracle_dgrad_full.argtypes = [u16p, u16p, u16p] + [i] * 10 + [f64p, i]
+    lib.oracle_dgrad_full.restype = i
+    lib.oracle_round_to_half.argtypes = [f64p, u16p, ctypes.c_int64]
+    lib.oracle_round_to_half.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i
+    return lib
+
+
+def load(path: str = LIB):
+    """Load the built oracle (building it only if no library exists)."""
+    global _lib
+    if path == LIB and _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        build(out=path)
+    lib = _bind(ctypes.CDLL(path))
+    if path == LIB:
+        _lib = lib
+    return lib
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float16:
+        raise TypeError("oracle inputs are float16 arrays")
+    return a.view(np.uint16), a.view(np.uint16).ctypes.data_as(ctypes.POINTER(ctypes.c_uint16))
+
+
+def out_extent(n_in, filt, stride, pad, lib=None):
+    return (lib or load()).oracle_out_extent(n_in, filt, stride, pad)
+
+
+def dgrad(dy, w, H, W, stride, pad, epilogue=EPI_NONE, z=None, rows=None,
+          threads=0, lib=None):
+    """fp64 dgrad of float16 dy [N,P,Q,K] and w [K,R,S,C].
+
+    Returns [N,H,W,C] float64, or [len(rows), C] when ``rows`` (linear pixel
+    indices (n*H+h)*W+w) is given.
+    """
+    lib = lib or load()
+    N, P, Q, K = dy.shape
+    K2, R, S, C = w.shape
+    if K2 != K:
+        raise ValueError("dy and w disagree on K")
+    if (lib.oracle_out_extent(H, R, stride, pad), lib.oracle_out_extent(W, S, stride, pad)) != (P, Q):
+        raise ValueError("dy spatial shape does not match H, W, R, S, stride, pad")
+    dyk, dyp = _u16(dy)
+    wk, wp = _u16(w)
+    zk = zp = None
+    if epilogue != EPI_NONE:
+        if z is None or tuple(z.shape) != (N, H, W, C):
+            raise ValueError("epilogue needs z of shape [N,H,W,C]")
+        zk, zp = _u16(z)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    if rows is None:
+        out = np.empty((N, H, W, C), dtype=np.float64)
+        rc = lib.oracle_dgrad_full(dyp, wp, zp, N, H, W, C, K, R, S, stride, pad,
+                                   epilogue, out.ctypes.data_as(f64p), int(threads))
+    else:
+        rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        out = np.empty((len(rr), C), dtype=np.float64)
+        rc = lib.oracle_dgrad_rows(dyp, wp, zp, N, H, W, C, K, R, S, stride, pad,
+                                   epilogue, rr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                   len(rr), out.ctypes.data_as(f64p), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_dgrad failed with code {rc}")
+    del dyk, wk, zk
+    return out
+
+
+def round_to_half(x, lib=None) -> np.ndarray:
+    """RNE fp16 encoding of an fp64 array, returned as float16."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.oracle_round_to_half(x.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                             out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), x.size)
+    return out.view(np.float16)
+
+
+def half_to_double(bits: int, lib=None) -> float:
+    return (lib or load()).oracle_half_to_double(bits)
+
+
+def hardswish_grad(zv: float, lib=None) -> float:
+    return (lib or load()).oracle_hardswish_grad(zv)
+
+
+def relu_grad(zv: float, lib=None) -> float:
+    return (lib or load()).oracle_relu_grad(zv)
+
+
+def max_threads(lib=None) -> int:
+    return (lib or load()).oracle_max_threads()

@@ -1,0 +1,366 @@
+"""Pins for the fp64 oracle: checks against what mathematics fixes, each
+independent of the oracle's own code path.
+
+Every ``check_*`` takes a loaded oracle library (``oracle.load(path)``) and
+raises AssertionError on a mismatch. ``tests/test_oracle.py`` runs them on the
+real oracle; ``tests/test_oracle_mutants.py`` runs them on deliberately broken
+copies of the oracle source and requires that at least one fails, so that a
+plausible mistake anywhere in the oracle is caught.
+
+Nothing here comes from the HIP path. The pages ("[CUTLASS] Conv2d dgrad",
+apache/tvm #10110, and the other pages) print no worked numerical example, so
+the fixed values below are derived by hand from the definition of dgrad as the
+adjoint of a strided, padded cross-correlation; each derivation is written out.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+import oracle
+
+# ----------------------------------------------------------------- helpers
+
+
+def f16(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float16)
+
+
+def forward_conv(x, w, stride, pad_h, pad_w=None):
+    """Forward cross-correlation by slicing a zero-padded input (fp64):
+    y[n,p,q,k] = sum_{r,t,c} xpad[n, p*s + r, q*s + t, c] * w[k,r,t,c]."""
+    if pad_w is None:
+        pad_w = pad_h
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    N, H, W, C = x.shape
+    K, R, S, C2 = w.shape
+    assert C == C2
+    P = (H + 2 * pad_h - R) // stride + 1
+    Q = (W + 2 * pad_w - S) // stride + 1
+    xp = np.zeros((N, H + 2 * pad_h, W + 2 * pad_w, C))
+    xp[:, pad_h:pad_h + H, pad_w:pad_w + W, :] = x
+    y = np.zeros((N, P, Q, K))
+    for r in range(R):
+        for t in range(S):
+            patch = xp[:, r:r + stride * (P - 1) + 1:stride, t:t + stride * (Q - 1) + 1:stride, :]
+            y += patch @ w[:, r, t, :].T
+    return y
+
+
+def scatter_dgrad(dy, w, H, W, stride, pad):
+    """Brute force in the scatter direction: every dy element pushes
+    dy[n,p,q,k] * w[k,r,t,:] to dx[n, p*s - pad + r, q*s - pad + t, :]
+    when that position exists. No division or modulo anywhere."""
+    dy = np.asarray(dy, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    N, P, Q, K = dy.shape
+    _, R, S, C = w.shape
+    dx = np.zeros((N, H, W, C))
+    for n in range(N):
+        for p in range(P):
+            for q in range(Q):
+                for r in range(R):
+                    h = p * stride - pad + r
+                    if h < 0 or h >= H:
+                        continue
+                    for t in range(S):
+                        x = q * stride - pad + t
+                        if x < 0 or x >= W:
+                            continue
+                        dx[n, h, x, :] += dy[n, p, q, :] @ w[:, r, t, :]
+    return dx
+
+
+def hardswish(z):
+    """hardswish(z) = z * min(max(z + 3, 0), 6) / 6 (textbook form)."""
+    return z * min(max(z + 3.0, 0.0), 6.0) / 6.0
+
+
+def _ext(n, f, s, p):
+    return (n + 2 * p - f) // s + 1
+
+
+# ----------------------------------------------------------------- pins
+
+W9 = np.arange(1, 10, dtype=np.float64).reshape(3, 3)   # [[1,2,3],[4,5,6],[7,8,9]]
+
+
+def check_fp16_decode(lib):
+    """Every one of the 65536 binary16 patterns decodes to numpy's value."""
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([lib.oracle_half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def check_fp16_rne_encode(lib):
+    """fp64 -> fp16 rounding equals numpy's correctly rounded (RNE) cast,
+    on random values across the range, exact ties, subnormals, overflow."""
+    rng = np.random.Generator(np.random.PCG64(3))
+    vals = [rng.standard_normal(4000) * s for s in (1e-6, 1e-3, 1.0, 100.0, 3e4)]
+    # exact ties: midpoints between neighbouring fp16 values
+    h = np.arange(0, 0x7bff, 7, dtype=np.uint16).view(np.float16).astype(np.float64)
+    hn = (np.arange(0, 0x7bff, 7, dtype=np.uint16) + 1).view(np.float16).astype(np.float64)
+    mids = (h + hn) / 2
+    specials = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 70000.0, -65520.0,
+                         2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 2049.0, 2051.0, -2051.0])
+    x = np.concatenate(vals + [mids, -mids, specials])
+    got = oracle.round_to_half(x, lib=lib)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+
+
+def check_out_extent(lib):
+    """P = floor((H + 2 pad - R)/s) + 1, spot values worked by hand."""
+    cases = {(56, 3, 2, 1): 28, (55, 3, 2, 1): 28, (56, 1, 2, 0): 28, (14, 3, 1, 1): 14,
+             (7, 3, 1, 1): 7, (4, 3, 2, 1): 2, (3, 3, 2, 1): 2, (2, 3, 1, 0): 0, (1, 1, 3, 0): 1}
+    for (n, f, s, p), want in cases.items():
+        assert lib.oracle_out_extent(n, f, s, p) == want, (n, f, s, p)
+
+
+def check_hand_examples(lib):
+    """E1-E4: one channel, hand-worked from the definition.
+
+    E1: 3x3 filter w = [[1,2,3],[4,5,6],[7,8,9]], stride 1, pad 1, H=W=3,
+        dy = all ones (P=Q=3). dx[h,x] sums w[r,t] over r with 0 <= h+1-r < 3
+        and t with 0 <= x+1-t < 3:
+          corner (0,0): r,t in {0,1} -> 1+2+4+5 = 12
+          edge   (0,1): r in {0,1}, t in {0,1,2} -> 1+2+3+4+5+6 = 21
+          corner (0,2): r in {0,1}, t in {1,2} -> 2+3+5+6 = 16
+          centre (1,1): all nine -> 45 ... and so on by symmetry.
+        A filter-flip mistake gives 28 at (0,0) instead.
+    E2: same w, one-hot dy at (1,1): dx[h,x] = w[h+1-1, x+1-1] = w[h,x], so dx = w.
+        One-hot at (0,0): dx[h,x] = w[h+1, x+1] where defined -> [[5,6,0],[8,9,0],[0,0,0]].
+    E3: stride 2, pad 1, H=W=4 (P=Q=2), dy = [[1,2],[3,4]].
+        Row h takes taps r = h + 1 - 2p: h=0 -> (p=0,r=1); h=1 -> (p=0,r=2),(p=1,r=0);
+        h=2 -> (p=1,r=1); h=3 -> (p=1,r=2). Columns likewise. E.g.
+        dx[1,1] = sum over p,q in {0,1}: dy[p,q] * w[2-2p, 2-2q]
+                = 1*9 + 2*7 + 3*3 + 4*1 = 36.
+        With H=W=3 (still P=Q=2) dx is the top-left 3x3 block.
+    E4: 1x1 filter w = 2, stride 2, pad 0, H=W=4, dy = [[1,2],[3,4]]:
+        only even (h,x) are reached: dx[2p,2q] = 2*dy[p,q], zeros elsewhere.
+    """
+    w = f16(W9.reshape(1, 3, 3, 1))
+    e1 = oracle.dgrad(f16(np.ones((1, 3, 3, 1))), w, 3, 3, 1, 1, lib=lib)[0, :, :, 0]
+    assert np.array_equal(e1, [[12, 21, 16], [27, 45, 33], [24, 39, 28]])
+
+    dy = np.zeros((1, 3, 3, 1))
+    dy[0, 1, 1, 0] = 1
+    assert np.array_equal(oracle.dgrad(f16(dy), w, 3, 3, 1, 1, lib=lib)[0, :, :, 0], W9)
+    dy = np.zeros((1, 3, 3, 1))
+    dy[0, 0, 0, 0] = 1
+    assert np.array_equal(oracle.dgrad(f16(dy), w, 3, 3, 1, 1, lib=lib)[0, :, :, 0],
+                          [[5, 6, 0], [8, 9, 0], [0, 0, 0]])
+
+    dy = f16(np.array([[1, 2], [3, 4]]).reshape(1, 2, 2, 1))
+    e3 = [[5, 14, 10, 12], [14, 36, 24, 30], [15, 34, 20, 24], [24, 55, 32, 36]]
+    assert np.array_equal(oracle.dgrad(dy, w, 4, 4, 2, 1, lib=lib)[0, :, :, 0], e3)
+    assert np.array_equal(oracle.dgrad(dy, w, 3, 3, 2, 1, lib=lib)[0, :, :, 0],
+                          np.array(e3)[:3, :3])
+
+    e4 = oracle.dgrad(dy, f16(np.full((1, 1, 1, 1), 2.0)), 4, 4, 2, 0, lib=lib)[0, :, :, 0]
+    assert np.array_equal(e4, [[2, 0, 4, 0], [0, 0, 0, 0], [6, 0, 8, 0], [0, 0, 0, 0]])
+
+
+def _scatter_cases():
+    """A structured sweep over (R, stride, pad, H) plus random shapes
+    covering N, W != H, S != R, C, K."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    cases = []
+    for R, s, pad, H in itertools.product((1, 2, 3), (1, 2, 3), (0, 1, 2), range(1, 7)):
+        S = int(rng.integers(1, 4))
+        W = int(rng.integers(1, 8))
+        N = int(rng.integers(1, 3))
+        C = int(rng.integers(1, 4))
+        K = int(rng.integers(1, 4))
+        cases.append((N, H, W, C, K, R, S, s, pad))
+    for _ in range(120):
+        R, S = (int(v) for v in rng.integers(1, 6, size=2))
+        s = int(rng.integers(1, 5))
+        pad = int(rng.integers(0, 3))
+        H, W = (int(v) for v in rng.integers(1, 10, size=2))
+        cases.append((int(rng.integers(1, 3)), H, W, int(rng.integers(1, 5)),
+                      int(rng.integers(1, 5)), R, S, s, pad))
+    return [c for c in cases if _ext(c[1], c[5], c[7], c[8]) >= 1 and _ext(c[2], c[6], c[7], c[8]) >= 1]
+
+
+def check_scatter_bruteforce(lib, cases=None):
+    """Integer-valued inputs: gather oracle == scatter brute force exactly."""
+    rng = np.random.Generator(np.random.PCG64(6))
+    for (N, H, W, C, K, R, S, s, pad) in (cases or _scatter_cases()):
+        P, Q = _ext(H, R, s, pad), _ext(W, S, s, pad)
+        dy = f16(rng.integers(-3, 4, size=(N, P, Q, K)))
+        w = f16(rng.integers(-3, 4, size=(K, R, S, C)))
+        got = oracle.dgrad(dy, w, H, W, s, pad, lib=lib)
+        ref = scatter_dgrad(dy, w, H, W, s, pad)
+        assert np.array_equal(got, ref), (N, H, W, C, K, R, S, s, pad)
+
+
+def check_adjoint_identity(lib):
+    """<fwd(x, w), dy> == <x, dgrad(dy, w)> to 1e-9 relative (fp64),
+    the forward computed by slicing a padded input."""
+    rng = np.random.Generator(np.random.PCG64(8))
+    shapes = [(2, 9, 7, 5, 6, 3, 3, 2, 1), (1, 8, 8, 8, 8, 3, 3, 1, 1), (2, 11, 10, 3, 4, 5, 3, 3, 2),
+              (1, 6, 9, 4, 4, 1, 1, 2, 0), (1, 7, 5, 2, 3, 2, 4, 2, 0), (3, 5, 5, 4, 2, 3, 3, 1, 0),
+              (1, 13, 13, 3, 3, 7, 7, 4, 3)]
+    for (N, H, W, C, K, R, S, s, pad) in shapes:
+        P, Q = _ext(H, R, s, pad), _ext(W, S, s, pad)
+        x = rng.standard_normal((N, H, W, C))
+        dy = f16(rng.standard_normal((N, P, Q, K)))
+        w = f16(rng.standard_normal((K, R, S, C)))
+        lhs = np.sum(forward_conv(x, w, s, pad) * dy.astype(np.float64))
+        rhs = np.sum(x * oracle.dgrad(dy, w, H, W, s, pad, lib=lib))
+        assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(lhs)), (lhs, rhs)
+
+
+def check_adjoint_unit_vectors(lib):
+    """Build the forward operator column by column from unit inputs e_i and
+    check dgrad(dy) == A^T dy entry by entry (the full transpose)."""
+    rng = np.random.Generator(np.random.PCG64(9))
+    for (N, H, W, C, K, R, S, s, pad) in [(1, 5, 4, 2, 3, 3, 2, 2, 1), (2, 4, 5, 2, 2, 3, 3, 1, 1),
+                                          (1, 6, 6, 1, 2, 2, 2, 3, 1)]:
+        P, Q = _ext(H, R, s, pad), _ext(W, S, s, pad)
+        w = f16(rng.standard_normal((K, R, S, C)))
+        dy = f16(rng.standard_normal((N, P, Q, K)))
+        nx = N * H * W * C
+        A = np.zeros((N * P * Q * K, nx))
+        for i in range(nx):
+            e = np.zeros(nx)
+            e[i] = 1.0
+            A[:, i] = forward_conv(e.reshape(N, H, W, C), w, s, pad).ravel()
+        ref = A.T @ dy.astype(np.float64).ravel()
+        got = oracle.dgrad(dy, w, H, W, s, pad, lib=lib).ravel()
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_matmul_special_cases(lib):
+    """1x1 filters: stride 1 is a plain matmul dy[M,K] @ w[K,C]; stride s
+    puts that product on the (s*p, s*q) lattice and zeros elsewhere."""
+    rng = np.random.Generator(np.random.PCG64(10))
+    N, H, W, C, K = 2, 5, 6, 7, 9
+    dy = f16(rng.standard_normal((N, H, W, K)))
+    w = f16(rng.standard_normal((K, 1, 1, C)))
+    got = oracle.dgrad(dy, w, H, W, 1, 0, lib=lib)
+    ref = (dy.astype(np.float64).reshape(-1, K) @ w.astype(np.float64).reshape(K, C)).reshape(N, H, W, C)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    for s, H, W in [(2, 7, 8), (3, 7, 9), (2, 6, 6)]:
+        P, Q = _ext(H, 1, s, 0), _ext(W, 1, s, 0)
+        dy = f16(rng.standard_normal((N, P, Q, K)))
+        got = oracle.dgrad(dy, w, H, W, s, 0, lib=lib)
+        ref = np.zeros((N, H, W, C))
+        ref[:, ::s, ::s, :][:, :P, :Q, :] = (dy.astype(np.float64).reshape(-1, K)
+                                             @ w.astype(np.float64).reshape(K, C)).reshape(N, P, Q, C)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+        mask = np.ones((H, W), bool)
+        mask[::s, ::s] = False
+        assert np.all(got[:, mask, :] == 0.0)
+
+
+def check_stride1_flipped_forward(lib):
+    """Stride 1: dgrad(dy, w, pad) is the forward correlation of dy with the
+    filter rotated 180 degrees and in/out channels swapped,
+    w'[c, r, t, k] = w[k, R-1-r, S-1-t, c], padded by R-1-pad and S-1-pad."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    for (N, H, W, C, K, R, S, pad) in [(2, 6, 7, 3, 4, 3, 3, 1), (1, 8, 5, 2, 5, 3, 2, 0),
+                                       (1, 9, 9, 4, 3, 5, 5, 2), (2, 5, 6, 3, 3, 4, 3, 1)]:
+        P, Q = _ext(H, R, 1, pad), _ext(W, S, 1, pad)
+        dy = f16(rng.standard_normal((N, P, Q, K)))
+        w = f16(rng.standard_normal((K, R, S, C)))
+        wflip = np.transpose(w.astype(np.float64)[:, ::-1, ::-1, :], (3, 1, 2, 0))
+        ref = forward_conv(dy, wflip, 1, R - 1 - pad, S - 1 - pad)
+        got = oracle.dgrad(dy, w, H, W, 1, pad, lib=lib)
+        assert got.shape == ref.shape
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_torch_conv2d_input(lib):
+    """Cross-check with PyTorch's CPU fp64 conv2d input gradient (NCHW)."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(13))
+    for (N, H, W, C, K, R, S, s, pad) in [(2, 9, 8, 5, 6, 3, 3, 2, 1), (1, 14, 14, 8, 8, 3, 3, 1, 1),
+                                          (2, 8, 8, 6, 4, 1, 1, 2, 0), (1, 11, 7, 3, 5, 5, 3, 3, 2),
+                                          (1, 10, 10, 4, 4, 3, 3, 2, 0)]:
+        P, Q = _ext(H, R, s, pad), _ext(W, S, s, pad)
+        dy = f16(rng.standard_normal((N, P, Q, K)))
+        w = f16(rng.standard_normal((K, R, S, C)))
+        ref = torch.nn.grad.conv2d_input(
+            (N, C, H, W),
+            torch.from_numpy(w.astype(np.float64)).permute(0, 3, 1, 2).contiguous(),
+            torch.from_numpy(dy.astype(np.float64)).permute(0, 3, 1, 2).contiguous(),
+            stride=s, padding=pad).permute(0, 2, 3, 1).numpy()
+        got = oracle.dgrad(dy, w, H, W, s, pad, lib=lib)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_epilogue_factors(lib):
+    """relu'(z) = [z > 0] (0 at z = 0); hardswish'(z) from the textbook
+    hardswish: 0 below -3, z/3 + 1/2 on [-3, 3] (closed, the reading at the
+    kinks), 1 above 3. Away from the kinks it must match central finite
+    differences of hardswish itself."""
+    for zv, g in [(-4, 0), (-3, -0.5), (-1.5, 0), (0, 0.5), (1.5, 1), (3, 1.5), (4, 1), (-3.5, 0), (10, 1)]:
+        assert lib.oracle_hardswish_grad(float(zv)) == g, zv
+    for zv, g in [(-1, 0), (0, 0), (-0.0, 0), (1e-8, 1), (2, 1)]:
+        assert lib.oracle_relu_grad(float(zv)) == g, zv
+    rng = np.random.Generator(np.random.PCG64(14))
+    hstep = 1e-5
+    for zv in rng.uniform(-6, 6, 400):
+        if min(abs(zv - 3), abs(zv + 3)) < 1e-3:
+            continue
+        fd = (hardswish(zv + hstep) - hardswish(zv - hstep)) / (2 * hstep)
+        assert abs(fd - lib.oracle_hardswish_grad(float(zv))) < 1e-6, zv
+
+
+def check_epilogue_applied(lib):
+    """dgrad with an epilogue equals plain dgrad times g(z) elementwise, with
+    g from the finite-difference-pinned closed forms above."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    N, H, W, C, K, R, S, s, pad = 2, 6, 5, 4, 3, 3, 3, 2, 1
+    P, Q = _ext(H, R, s, pad), _ext(W, S, s, pad)
+    dy = f16(rng.standard_normal((N, P, Q, K)))
+    w = f16(rng.standard_normal((K, R, S, C)))
+    z = f16(rng.choice([-4, -3, -1.5, -0.25, 0, 0.75, 1.5, 3, 4], size=(N, H, W, C)))
+    base = scatter_dgrad(dy, w, H, W, s, pad)
+    zz = z.astype(np.float64)
+    g_hs = np.where(zz < -3, 0.0, np.where(zz > 3, 1.0, zz / 3 + 0.5))
+    g_relu = (zz > 0).astype(np.float64)
+    assert np.allclose(oracle.dgrad(dy, w, H, W, s, pad, 2, z, lib=lib), base * g_hs, rtol=1e-12, atol=1e-12)
+    assert np.allclose(oracle.dgrad(dy, w, H, W, s, pad, 1, z, lib=lib), base * g_relu, rtol=1e-12, atol=1e-12)
+
+
+def check_rows_api(lib):
+    """Sampled-row evaluation equals the matching rows of the full tensor."""
+    rng = np.random.Generator(np.random.PCG64(16))
+    N, H, W, C, K, R, S, s, pad = 2, 7, 6, 5, 4, 3, 3, 2, 1
+    P, Q = _ext(H, R, s, pad), _ext(W, S, s, pad)
+    dy = f16(rng.standard_normal((N, P, Q, K)))
+    w = f16(rng.standard_normal((K, R, S, C)))
+    z = f16(rng.standard_normal((N, H, W, C)))
+    full = oracle.dgrad(dy, w, H, W, s, pad, 2, z, lib=lib).reshape(-1, C)
+    rows = rng.choice(N * H * W, size=20, replace=False)
+    part = oracle.dgrad(dy, w, H, W, s, pad, 2, z, rows=rows, lib=lib)
+    assert np.array_equal(part, full[rows])
+
+
+ALL_CHECKS = [
+    check_fp16_decode, check_fp16_rne_encode, check_out_extent, check_hand_examples,
+    check_scatter_bruteforce, check_adjoint_identity, check_adjoint_unit_vectors,
+    check_matmul_special_cases, check_stride1_flipped_forward, check_torch_conv2d_input,
+    check_epilogue_factors, check_epilogue_applied, check_rows_api,
+]
+
+
+def run_all(lib) -> list:
+    """Run every pin; return the names of those that failed (or raised)."""
+    failed = []
+    for chk in ALL_CHECKS:
+        try:
+            chk(lib)
+        except Exception as e:  # noqa: BLE001 - a mutant may fail in any way
+            failed.append(f"{chk.__name__}: {type(e).__name__}")
+    return failed
