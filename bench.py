@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the conv2d dgrad hot path on one MI355X.
+
+A step is one pass over the measured ResNet-50 dgrad suite: the batch-8
+stage-2 3x3 layer and the batch-256 layers (3x3 stride 2, the 1x1 stride-2
+downsample, the 1x1 stride-1 reduce, and the stage-4 3x3 with the fused
+hardswish' epilogue), each a single call of the C ABI on synthetic seeded
+inputs already resident in HBM. That covers every part of the path: the
+stride-phase plan, zero phases, the MFMA implicit GEMM, the fused epilogue
+and the tile-config table (filled during warm-up).
+
+value = useful FLOPs of the suite (2*N*P*Q*K*C*R*S per layer) / time per step.
+
+Prints one JSON line (see the fields at the end of main()).
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-fraction F]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import CONFIGS, EPI_NAMES, make_inputs  # noqa: E402
+
+SUITE = [1, 2, 3, 4, 5]            # indices into CONFIGS; 0 is the latency-sized parity case
+MFMA_PEAK_TFLOPS = 2500.0          # MI355X dense fp16 matrix-core peak
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
+RIDGE = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
+METRIC = "dgrad TFLOP/s and % of fp16 MFMA peak, ResNet-50 layer shapes at N=8/256"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def roofline_of(cfg, seconds):
+    flops = cfg.useful_flops()
+    nbytes = cfg.algorithmic_bytes()
+    ai = flops / nbytes
+    if ai >= RIDGE:
+        achieved = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_PEAK_TFLOPS}
+    achieved = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS}
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when
+    it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "convolution_backward_amd", "csrc", "dgrad_kernels.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if t.get("kernel_source_sha256_16") != digest:
+        return None
+    entry = t.get("layers", {}).get(kernel_key)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def cpu_baseline(inputs, fraction, seed=99):
+    """The oracle, untuned, on a seeded `fraction` of each layer's output
+    pixels; the full-suite time is extrapolated by 1/fraction per layer."""
+    import oracle
+    lib = oracle.load()
+    threads = oracle.max_threads(lib)
+    total_t = 0.0
+    rows_done = 0
+    for idx in SUITE:
+        cfg = CONFIGS[idx]
+        npix = cfg.N * cfg.H * cfg.W
+        k = max(1, int(round(npix * fraction)))
+        rng = np.random.Generator(np.random.PCG64(seed + idx))
+        rows = np.sort(rng.choice(npix, size=k, replace=False))
+        inp = inputs[idx]
+        t0 = time.perf_counter()
+        oracle.dgrad(inp["dy"], inp["w"], cfg.H, cfg.W, cfg.stride, cfg.pad, cfg.epilogue, inp["z"],
+                     rows=rows, lib=lib)
+        dt = time.perf_counter() - t0
+        total_t += dt * npix / k
+        rows_done += k
+        log(f"[cpu] {cfg.name}: {k} of {npix} pixels in {dt:.2f} s")
+    flops = sum(CONFIGS[i].useful_flops() for i in SUITE)
+    return {"value": flops / total_t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"seeded {fraction:.0%} of the output pixels of each suite layer "
+                      f"({rows_done} pixel rows, all channels, fp64); full-suite time extrapolated "
+                      f"per layer by pixel count: {total_t:.1f} s per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-fraction", type=float, default=0.5,
+                    help="share of each layer's pixels the oracle computes for cpu_baseline (0 skips it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this library has no multi-GPU path: "
+              "dgrad shards over the batch with no exchange, so N GPUs run N independent copies.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import convolution_backward_amd as cb
+    cb.get_lib()    # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, resident in HBM before timing
+    host_inputs, layers = {}, []
+    for idx in SUITE:
+        cfg = CONFIGS[idx]
+        inp = make_inputs(cfg)
+        host_inputs[idx] = inp
+        d = {k: (None if v is None else torch.from_numpy(v).to(dev)) for k, v in inp.items()}
+        d["dx"] = torch.empty((cfg.N, cfg.H, cfg.W, cfg.C), dtype=torch.float16, device=dev)
+        layers.append((cfg, d))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def one_layer(cfg, d):
+        cb.conv2d_dgrad_nhwc(d["dy"], d["w"], d["dx"], cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
+                             cfg.stride, cfg.pad, cfg.epilogue, d["z"], stream.cuda_stream)
+
+    # ---- warm-up (the first call per layer fills the tile-config table)
+    for _ in range(args.warmup):
+        for cfg, d in layers:
+            one_layer(cfg, d)
+    torch.cuda.synchronize()
+
+    # ---- timed steps; per-layer HIP events on the launch stream
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in layers] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for li, (cfg, d) in enumerate(layers):
+            ev[s][li][0].record(stream)
+            one_layer(cfg, d)
+            ev[s][li][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per_layer = []
+    for li, (cfg, d) in enumerate(layers):
+        ms = [ev[s][li][0].elapsed_time(ev[s][li][1]) for s in range(args.steps)]
+        avg = float(np.mean(ms))
+        cid, _ = cb.conv2d_dgrad_query_config(cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S, cfg.stride,
+                                              cfg.pad, cfg.epilogue)
+        rl = roofline_of(cfg, avg * 1e-3)
+        per_layer.append({
+            "layer": cfg.name, "avg_us": avg * 1e3, "min_us": float(np.min(ms)) * 1e3,
+            "tflops": cfg.useful_flops() / (avg * 1e-3) / 1e12,
+            "mfma_frac": cfg.useful_flops() / (avg * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+            "alg_gbs": cfg.algorithmic_bytes() / (avg * 1e-3) / 1e9,
+            "hbm_frac": cfg.algorithmic_bytes() / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bound": rl["bound"], "roofline_frac": rl["frac"],
+            "tile_config": cb.conv2d_dgrad_config_name(cid),
+            "useful_gflop": cfg.useful_flops() / 1e9, "alg_mb": cfg.algorithmic_bytes() / 1e6,
+        })
+        log(f"[gpu] {cfg.name:34s} {avg*1e3:9.2f} us  {per_layer[-1]['tflops']:7.1f} TFLOP/s  "
+            f"{per_layer[-1]['alg_gbs']:7.0f} GB/s  {rl['bound']} {rl['frac']:.1%}  [{per_layer[-1]['tile_config']}]")
+
+    flops = sum(cfg.useful_flops() for cfg, _ in layers)
+    kernel_ms = sum(p["avg_us"] for p in per_layer) / 1e3
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    dom = max(range(len(layers)), key=lambda i: per_layer[i]["avg_us"])
+    dcfg = layers[dom][0]
+    roof = roofline_of(dcfg, per_layer[dom]["avg_us"] * 1e-6)
+    roof["kernel"] = f"dgrad_igemm<{per_layer[dom]['tile_config']}> on {dcfg.name}"
+    roof["traffic"] = measured_traffic(dcfg.name)
+
+    cpu = None
+    if args.cpu_fraction > 0:
+        cpu = cpu_baseline(host_inputs, args.cpu_fraction)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "resnet50_dgrad_suite: " + ", ".join(
+                f"{c.name} (N={c.N} {c.H}x{c.W} C={c.C} K={c.K} {c.R}x{c.S} s{c.stride} p{c.pad}"
+                f"{'' if c.epilogue == 0 else ' +' + EPI_NAMES[c.epilogue]})" for c, _ in layers),
+            "accumulate": "f32",
+            "layout": "NHWC fp16 dy/dx/z, KRSC fp16 filter",
+            "useful_gflop_per_step": flops / 1e9,
+        },
+        "mfma_frac_of_peak": value / MFMA_PEAK_TFLOPS,
+        "kernel_ms_per_step": kernel_ms,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layers": per_layer,
+        "device": torch.cuda.get_device_name(dev),
+        "build": cb.conv2d_dgrad_build_info(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

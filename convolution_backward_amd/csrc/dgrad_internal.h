@@ -1,0 +1,57 @@
+// Internal interface between the host launcher (dgrad_api.cpp) and the HIP
+// kernels (dgrad_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "fastdiv.h"
+
+namespace cbw {
+
+// Phases per launch; strides above 4 are split over several launches.
+constexpr int kMaxPhasesPerLaunch = 16;
+
+// One stride phase as the kernel sees it (see dgrad_plan.h for the algebra).
+struct PhaseArg {
+    int ph, pw;          // lattice offsets
+    int Wp;              // lattice width
+    int nr, nt;          // tap counts (0: zero phase)
+    int r0, t0;          // first taps
+    int dr0, dt0;        // dy offsets of the first taps
+    int M;               // N*Hp*Wp
+    int tile_begin;      // first tile id of this phase in the launch
+    FastDiv div_hw;      // division by Hp*Wp
+    FastDiv div_w;       // division by Wp
+};
+
+struct KernelArgs {
+    const uint16_t* dy;
+    const uint16_t* w;
+    uint16_t* dx;
+    const uint16_t* z;
+    int H, W, C, K, R, S, P, Q;
+    int stride;
+    int epi;
+    int tiles_n;         // tiles along C
+    int total_tiles;     // grid size
+    int group;           // consecutive tiles kept on one XCD
+    int nphases;
+    PhaseArg ph[kMaxPhasesPerLaunch];
+};
+
+struct TileConfig {
+    int BM;              // dx pixels per tile (GEMM rows)
+    int BN;              // dx channels per tile (GEMM columns)
+    int BK;              // reduction slice per pipeline stage
+    int WM, WN;          // wave grid (64-lane waves) over the tile
+    const char* name;
+    int lds_bytes;
+};
+
+int num_tile_configs();
+const TileConfig& tile_config(int id);
+hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);
+
+}  // namespace cbw

@@ -1,0 +1,170 @@
+/*
+ * conv2d_dgrad.h -- C ABI of the MI355X (gfx950) conv2d backward-data library.
+ *
+ * The operation. The forward layer is a 2-D cross-correlation with one stride
+ * s and one symmetric zero padding `pad`:
+ *     y[n,p,q,k] = sum_{r,t,c} x[n, p*s - pad + r, q*s - pad + t, c] * w[k,r,t,c]
+ * with P = floor((H + 2*pad - R)/s) + 1 and Q = floor((W + 2*pad - S)/s) + 1.
+ * Backward-data ("dgrad", the subject of "[CUTLASS] Conv2d dgrad", apache/tvm
+ * PR #10110, and of cuDNN's ConvolutionBackwardData in "Performance
+ * improvements by calling cuDNN API", JuliaGPU/CUDA.jl PR #321) is its adjoint:
+ *     dx[n,h,w,c] = sum_{k,r,t} dy[n,p,q,k] * w[k,r,t,c]
+ * over the taps where h = p*s - pad + r and w = q*s - pad + t for some
+ * 0 <= p < P, 0 <= q < Q. Positions that no tap reaches are written as 0.
+ * It is computed as an implicit GEMM with M = N*H*W rows, C columns and a
+ * reduction over K*R*S, split for stride s into s*s phase sub-GEMMs so that no
+ * inserted-zero products are formed.
+ *
+ * Precision. fp16 storage, fp32 accumulation (the tvm PR's review remarks that
+ * training needs fp32 accumulation), one round-to-nearest-even conversion to
+ * fp16 at the end.
+ *
+ * Fused epilogue (the fusion the tvm PR notes is "not enabled for dgrad yet",
+ * and the Conv2D + BiasAdd + Hardswish pattern of the Bolt paper notes,
+ * KuangjuX/Paper-reading #28, "Insights"): dx = acc * g(z) with z the saved
+ * pre-activation, g = relu'(z) = [z > 0] or g = hardswish'(z) = 0 (z < -3),
+ * z/3 + 1/2 (-3 <= z <= 3), 1 (z > 3). g is evaluated in fp32.
+ *
+ * Layouts (all C-contiguous fp16, i.e. IEEE binary16 bit patterns):
+ *     dy [N][P][Q][K]   NHWC gradient of the forward output
+ *     w  [K][R][S][C]   KRSC filter (k = output channel of the forward layer)
+ *     dx [N][H][W][C]   NHWC result; write-only, every element overwritten
+ *     z  [N][H][W][C]   NHWC saved pre-activation (epilogue only)
+ *
+ * Ownership and execution. All tensor pointers are device pointers owned by
+ * the caller, who keeps them alive until the enqueued work completes. Calls
+ * are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ * The library allocates no device memory and needs no workspace. dx is never
+ * read (it may hold anything, NaN included, before the call). dx must not
+ * overlap dy, w or z.
+ *
+ * Tile-config selection. The first call for a new problem key (every shape
+ * argument, the epilogue kind and the device) picks a tile configuration:
+ * when autotuning is on and the stream is not capturing, every compiled
+ * candidate is timed on the caller's own buffers and stream (the "Find"
+ * approach described in the CUDA.jl PR; this call then synchronises the
+ * stream once); otherwise a shape heuristic picks one (the "Get" approach).
+ * The choice is cached in an unbounded, mutex-guarded table (that PR's final
+ * choice: a plain dictionary without a capacity limit, keyed by the full
+ * problem) and reused by every later call with the same key.
+ *
+ * Errors. Every entry point returns a status code. Arguments are validated
+ * before any HIP call; on failure nothing is enqueued and
+ * conv2d_dgrad_last_error() (per thread) describes the problem.
+ */
+#ifndef CONV2D_DGRAD_H
+#define CONV2D_DGRAD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define CONV2D_DGRAD_OK 0
+#define CONV2D_DGRAD_INVALID_ARGUMENT 1 /* null pointer, dim < 1, stride < 1, pad < 0,
+                                           P or Q < 1, unknown epilogue, z missing,
+                                           pointer not 16-byte aligned, dx overlapping
+                                           an input, bad config id */
+#define CONV2D_DGRAD_UNSUPPORTED 2      /* C or K not a multiple of 8, a tensor of
+                                           2^31 elements or more, stride > 16 */
+#define CONV2D_DGRAD_HIP_ERROR 3        /* a HIP runtime call or launch failed */
+
+/* epilogue kinds */
+#define CONV2D_DGRAD_EPI_NONE 0
+#define CONV2D_DGRAD_EPI_DRELU 1
+#define CONV2D_DGRAD_EPI_DHARDSWISH 2
+
+/*
+ * dx = dgrad(dy, w) [* g(z)] on `stream`.
+ *   N, H, W, C : batch, dx height, dx width, dx channels
+ *   K, R, S    : dy channels, filter height, filter width
+ *   stride, pad: the forward layer's stride (1..16) and symmetric padding (>= 0)
+ *   epilogue   : CONV2D_DGRAD_EPI_*; z must be non-NULL unless NONE (ignored then)
+ * P and Q are derived from H, W, R, S, stride and pad as above (several H give
+ * the same P under stride > 1, which is why H and W are passed).
+ * Constraints: C % 8 == 0, K % 8 == 0 (16-byte vectors along channels), all
+ * pointers 16-byte aligned, every tensor below 2^31 elements.
+ */
+int conv2d_dgrad_nhwc(const void* dy, const void* w, void* dx,
+                      int N, int H, int W, int C, int K, int R, int S,
+                      int stride, int pad, int epilogue, const void* z,
+                      void* stream);
+
+/*
+ * Same computation with an explicit tile configuration (0 <= config_id <
+ * conv2d_dgrad_num_configs()), bypassing the table. For tests that check
+ * every candidate and for benchmarks that sweep them.
+ */
+int conv2d_dgrad_nhwc_config(const void* dy, const void* w, void* dx,
+                             int N, int H, int W, int C, int K, int R, int S,
+                             int stride, int pad, int epilogue, const void* z,
+                             int config_id, void* stream);
+
+/* Number of compiled tile configurations, and a readable name for one
+ * ("BMxBNxBK/WMxWN"): buf receives at most buflen bytes, NUL-terminated. */
+int conv2d_dgrad_num_configs(void);
+int conv2d_dgrad_config_name(int config_id, char* buf, int buflen);
+
+/*
+ * The configuration the table holds for a problem key, without launching:
+ * *config_id = the cached choice, or the heuristic's choice when the key is
+ * not cached (*cached = 0). Validates like conv2d_dgrad_nhwc. Needs no GPU
+ * when the key is not cached.
+ */
+int conv2d_dgrad_query_config(int N, int H, int W, int C, int K, int R, int S,
+                              int stride, int pad, int epilogue,
+                              int* config_id, int* cached);
+
+/* Autotuning on (1, the default unless the environment sets
+ * CONV2D_DGRAD_AUTOTUNE=0) or off (0). Returns the previous setting. */
+int conv2d_dgrad_set_autotune(int on);
+
+/* Drop every cached choice; number of entries in the table. */
+int conv2d_dgrad_cache_clear(void);
+int conv2d_dgrad_cache_size(void);
+
+/* Persist the table to a text file / merge a saved table into it (so a new
+ * process skips re-profiling). Lines: the key fields, then the config name. */
+int conv2d_dgrad_cache_save(const char* path);
+int conv2d_dgrad_cache_load(const char* path);
+
+/*
+ * The stride-phase plan (host-only, no GPU): for each phase (ph, pw) in
+ * [0,s)^2 the output positions h = ph + s*i, w = pw + s*j form an Hp x Wp
+ * sub-grid, and only the filter taps r = r0 + a*s (a < nr), t = t0 + b*s
+ * (b < nt) reach it, from dy rows p = i + dr0 - a and columns q = j + dt0 - b.
+ * Each phase is an M x C x Kg GEMM with M = N*Hp*Wp and Kg = K*nr*nt; Kg == 0
+ * marks a zero phase, whose outputs are all exact zeros. Phases with an empty
+ * sub-grid (Hp or Wp == 0, possible when s > H or s > W) are omitted.
+ * Phases are returned heaviest first (by nr*nt, ties by (ph, pw)).
+ */
+typedef struct {
+    int ph, pw;      /* phase offsets in [0, stride) */
+    int Hp, Wp;      /* sub-grid extents */
+    int r0, t0;      /* first row tap, first column tap */
+    int nr, nt;      /* number of row taps and column taps */
+    int dr0, dt0;    /* dy row/column offsets of the first taps */
+    long long M;     /* GEMM rows N*Hp*Wp */
+    long long Kg;    /* GEMM reduction length K*nr*nt (0: zero phase) */
+} conv2d_dgrad_phase;
+
+int conv2d_dgrad_plan(int N, int H, int W, int C, int K, int R, int S,
+                      int stride, int pad, conv2d_dgrad_phase* phases,
+                      int max_phases, int* nphases, int* P, int* Q);
+
+/* Validation alone (no HIP call): the status conv2d_dgrad_nhwc would return
+ * for these arguments before launching anything. */
+int conv2d_dgrad_check(const void* dy, const void* w, void* dx,
+                       int N, int H, int W, int C, int K, int R, int S,
+                       int stride, int pad, int epilogue, const void* z);
+
+/* Thread-local text of the last error ("" if none). */
+const char* conv2d_dgrad_last_error(void);
+
+/* Compiler and HIP versions the library was built with, and its target. */
+const char* conv2d_dgrad_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CONV2D_DGRAD_H */

@@ -1,0 +1,184 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+validates arguments before any HIP call, and plans stride phases correctly.
+No test here launches a kernel."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import convolution_backward_amd as cb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv2d_dgrad.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(conv2d_dgrad_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(cb.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_status_codes_match_binding():
+    text = open(HEADER).read()
+    for name, val in [("OK", cb.OK), ("INVALID_ARGUMENT", cb.INVALID_ARGUMENT),
+                      ("UNSUPPORTED", cb.UNSUPPORTED), ("HIP_ERROR", cb.HIP_ERROR),
+                      ("EPI_NONE", cb.EPI_NONE), ("EPI_DRELU", cb.EPI_DRELU),
+                      ("EPI_DHARDSWISH", cb.EPI_DHARDSWISH)]:
+        m = re.search(rf"#define CONV2D_DGRAD_{name} (\d+)", text)
+        assert m and int(m.group(1)) == val, name
+
+
+def test_build_info_names_target():
+    info = cb.conv2d_dgrad_build_info()
+    assert "gfx950" in info and "HIP" in info
+
+
+def test_config_names():
+    n = cb.conv2d_dgrad_num_configs()
+    assert n >= 4
+    names = [cb.conv2d_dgrad_config_name(i) for i in range(n)]
+    assert len(set(names)) == n
+    for nm in names:
+        assert re.fullmatch(r"\d+x\d+x\d+/\d+x\d+", nm)
+    with pytest.raises(cb.DgradError):
+        cb.conv2d_dgrad_config_name(n)
+
+
+# Fake, aligned, non-overlapping addresses: validation never dereferences them.
+DY, WP, DX, Z = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+GOOD = dict(N=2, H=8, W=8, C=16, K=8, R=3, S=3, stride=2, pad=1)
+
+
+def check(dy=DY, w=WP, dx=DX, z=None, epi=0, **kw):
+    args = dict(GOOD)
+    args.update(kw)
+    return cb.conv2d_dgrad_check(dy, w, dx, args["N"], args["H"], args["W"], args["C"], args["K"],
+                                 args["R"], args["S"], args["stride"], args["pad"], epi, z)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, cb.OK),
+    ({"N": 0}, cb.INVALID_ARGUMENT), ({"H": 0}, cb.INVALID_ARGUMENT), ({"C": -8}, cb.INVALID_ARGUMENT),
+    ({"R": 0}, cb.INVALID_ARGUMENT), ({"stride": 0}, cb.INVALID_ARGUMENT), ({"pad": -1}, cb.INVALID_ARGUMENT),
+    ({"H": 1, "R": 5, "pad": 0}, cb.INVALID_ARGUMENT),             # P < 1
+    ({"epi": 7}, cb.INVALID_ARGUMENT), ({"epi": cb.EPI_DHARDSWISH}, cb.INVALID_ARGUMENT),  # z missing
+    ({"epi": cb.EPI_DRELU, "z": Z}, cb.OK),
+    ({"dy": 0}, cb.INVALID_ARGUMENT), ({"dx": 0}, cb.INVALID_ARGUMENT), ({"w": 0}, cb.INVALID_ARGUMENT),
+    ({"dy": DY + 8}, cb.INVALID_ARGUMENT),                           # misaligned
+    ({"dx": DY + 16}, cb.INVALID_ARGUMENT),                          # dx overlaps dy
+    ({"C": 12}, cb.UNSUPPORTED), ({"K": 4}, cb.UNSUPPORTED), ({"stride": 17, "H": 40, "W": 40}, cb.UNSUPPORTED),
+    ({"N": 70000, "H": 200, "W": 200}, cb.UNSUPPORTED),               # 2^31 elements
+])
+def test_validation_codes(kw, code):
+    assert check(**kw) == code
+    if code != cb.OK:
+        assert cb.conv2d_dgrad_last_error() != ""
+
+
+def test_invalid_call_returns_before_any_hip_call():
+    # conv2d_dgrad_nhwc with a bad argument fails with the validation code,
+    # not a HIP error, on a host without a GPU.
+    with pytest.raises(cb.DgradError) as e:
+        cb.conv2d_dgrad_nhwc(DY, WP, DX, 2, 8, 8, 12, 8, 3, 3, 1, 1, stream=0)
+    assert e.value.code == cb.UNSUPPORTED
+    with pytest.raises(cb.DgradError) as e:
+        cb.conv2d_dgrad_nhwc_config(DY, WP, DX, 2, 8, 8, 16, 8, 3, 3, 1, 1, config_id=99, stream=0)
+    assert e.value.code == cb.INVALID_ARGUMENT
+
+
+def brute_phase(H, R, stride, pad, ph):
+    """Taps reaching output rows h = ph + s*i, found by trying every r."""
+    rows = list(range(ph, H, stride))
+    taps = [r for r in range(R) if (ph + pad - r) % stride == 0]
+    deltas = [(ph + pad - r) // stride for r in taps]
+    return len(rows), taps, deltas
+
+
+@pytest.mark.parametrize("stride", [1, 2, 3, 4, 5])
+def test_plan_matches_brute_force(stride):
+    for H, W, R, S, pad in itertools.product(range(1, 9), (3, 7), (1, 2, 3, 5), (1, 3), (0, 1, 2, 3)):
+        if (H + 2 * pad - R) < 0 or (W + 2 * pad - S) < 0:
+            continue
+        N, K = 2, 8
+        P, Q, phases = cb.conv2d_dgrad_plan(N, H, W, 8, K, R, S, stride, pad)
+        assert P == (H + 2 * pad - R) // stride + 1 and Q == (W + 2 * pad - S) // stride + 1
+        seen = set()
+        for p in phases:
+            hp, rt, rd = brute_phase(H, R, stride, pad, p["ph"])
+            wp, tt, td = brute_phase(W, S, stride, pad, p["pw"])
+            assert (p["Hp"], p["Wp"]) == (hp, wp)
+            assert [p["r0"] + a * stride for a in range(p["nr"])] == rt
+            assert [p["t0"] + b * stride for b in range(p["nt"])] == tt
+            assert [p["dr0"] - a for a in range(p["nr"])] == rd
+            assert [p["dt0"] - b for b in range(p["nt"])] == td
+            assert p["M"] == N * hp * wp and p["Kg"] == K * len(rt) * len(tt)
+            seen.add((p["ph"], p["pw"]))
+        # every non-empty lattice appears once; lattices cover dx exactly
+        want = {(a, b) for a in range(min(stride, H)) for b in range(min(stride, W))}
+        assert seen == want
+        assert sum(p["M"] for p in phases) == N * H * W
+        # heaviest first
+        taps = [p["nr"] * p["nt"] for p in phases]
+        assert taps == sorted(taps, reverse=True)
+
+
+def test_plan_of_measured_layers():
+    from workloads import CONFIGS
+    c = CONFIGS[2]   # 3x3, stride 2, pad 1 on 56x56
+    P, Q, phases = cb.conv2d_dgrad_plan(c.N, c.H, c.W, c.C, c.K, c.R, c.S, c.stride, c.pad)
+    assert (P, Q) == (28, 28)
+    assert [p["nr"] * p["nt"] for p in phases] == [4, 2, 2, 1]
+    assert all(p["M"] == 256 * 28 * 28 for p in phases)
+    c = CONFIGS[3]   # 1x1, stride 2: one GEMM phase, three zero phases
+    _, _, phases = cb.conv2d_dgrad_plan(c.N, c.H, c.W, c.C, c.K, c.R, c.S, c.stride, c.pad)
+    assert [p["Kg"] for p in phases] == [512, 0, 0, 0]
+    assert (phases[0]["ph"], phases[0]["pw"]) == (0, 0)
+
+
+def test_query_config_without_gpu_uses_heuristic():
+    cid, cached = cb.conv2d_dgrad_query_config(8, 56, 56, 64, 64, 3, 3, 1, 1)
+    assert 0 <= cid < cb.conv2d_dgrad_num_configs() and not cached
+    assert "x64x" in cb.conv2d_dgrad_config_name(cid)   # narrow layer -> 64-channel tile
+
+
+def test_cache_save_load_roundtrip(tmp_path):
+    cb.conv2d_dgrad_cache_clear()
+    assert cb.conv2d_dgrad_cache_size() == 0
+    # A saved line for a CPU-only host ("none", 256 CUs) is what a query here looks up.
+    name = cb.conv2d_dgrad_config_name(1)
+    f = tmp_path / "table.txt"
+    f.write_text(f"2 8 8 16 8 3 3 2 1 0 none 256 {name}\nthis line is ignored\n")
+    cb.conv2d_dgrad_cache_load(str(f))
+    assert cb.conv2d_dgrad_cache_size() == 1
+    cid, cached = cb.conv2d_dgrad_query_config(2, 8, 8, 16, 8, 3, 3, 2, 1)
+    assert cached and cid == 1
+    out = tmp_path / "saved.txt"
+    cb.conv2d_dgrad_cache_save(str(out))
+    assert out.read_text().split() == f"2 8 8 16 8 3 3 2 1 0 none 256 {name}".split()
+    cb.conv2d_dgrad_cache_clear()
+    assert cb.conv2d_dgrad_cache_size() == 0
+
+
+def test_autotune_toggle():
+    prev = cb.conv2d_dgrad_set_autotune(False)
+    assert cb.conv2d_dgrad_set_autotune(prev) is False
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import importlib
+    mod = importlib.import_module("convolution_backward_amd")
+    monkeypatch.setattr(mod, "_lib", None)
+    monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        mod.get_lib()

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path against the fp64 oracle, through the C ABI.
+
+Tolerance: |gpu - ref| <= 1e-3 + 1e-2 |ref| elementwise; bit-exact where the
+arithmetic is exact (integer inputs, zero phases, one-hot dy, epilogue ties).
+dx is filled with NaN before every call so an unwritten element fails.
+"""
+import numpy as np
+import pytest
+
+import convolution_backward_amd as cb
+import oracle
+from workloads import (CONFIGS, EPI_DHARDSWISH, EPI_DRELU, EPI_NONE, integer_inputs, make_inputs,
+                       one_hot_dy, small_config)
+from tests.gpu_util import assert_close, note, ref_full, ref_rows, run, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+# N, H, W, C, K, R, S, stride, pad: several tiles, ragged tails in M, C and K,
+# every stride-phase situation (zero phases, empty lattices, >16 phases).
+SMALL = [
+    (2, 15, 13, 136, 72, 3, 3, 1, 1),
+    (2, 17, 16, 64, 128, 3, 3, 2, 1),
+    (3, 11, 12, 40, 24, 3, 3, 2, 0),
+    (1, 20, 19, 32, 16, 1, 1, 2, 0),
+    (2, 9, 9, 16, 16, 5, 5, 3, 2),
+    (1, 14, 14, 264, 56, 1, 1, 1, 0),
+    (2, 8, 10, 24, 8, 2, 4, 2, 1),
+    (1, 23, 23, 16, 16, 3, 3, 5, 1),
+    (1, 5, 5, 8, 8, 7, 7, 1, 3),
+    (1, 1, 1, 8, 8, 1, 1, 1, 0),
+    (1, 3, 3, 8, 8, 3, 3, 4, 2),
+    (1, 33, 35, 8, 8, 3, 3, 16, 1),
+    (4, 28, 28, 192, 320, 3, 3, 1, 1),
+]
+
+
+def _cfg(shape, epi=EPI_NONE, seed=7):
+    return small_config(*shape, epilogue=epi, seed=seed)
+
+
+@pytest.fixture(scope="module")
+def small_refs():
+    out = {}
+    for shape in SMALL:
+        for epi in (EPI_NONE, EPI_DRELU, EPI_DHARDSWISH):
+            cfg = _cfg(shape, epi)
+            inp = make_inputs(cfg)
+            out[(shape, epi)] = (cfg, inp, ref_full(cfg, inp))
+    return out
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_every_config(small_refs, shape):
+    cfg, inp, ref = small_refs[(shape, EPI_NONE)]
+    for cid in range(cb.conv2d_dgrad_num_configs()):
+        note(f"small {shape} config {cid} {cb.conv2d_dgrad_config_name(cid)}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} config {cid}")
+
+
+@pytest.mark.parametrize("epi", [EPI_DRELU, EPI_DHARDSWISH])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_epilogues(small_refs, shape, epi):
+    cfg, inp, ref = small_refs[(shape, epi)]
+    note(f"small {shape} epilogue {epi} (selected config)")
+    assert_close(run(cfg, inp), ref, f"{shape} epi {epi}")
+    note(f"small {shape} epilogue {epi} config 0")
+    assert_close(run(cfg, inp, config_id=0), ref, f"{shape} epi {epi} config 0")
+
+
+# ---------------------------------------------------------------- full sizes
+
+@pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
+def test_measured_layer(idx):
+    """Each measured layer at full size, in the configuration the table picks
+    (the one bench.py times): full comparison where the oracle is quick,
+    else a seeded sample of pixels plus every corner/edge pixel of the first
+    and last image. The whole tensor is checked for unwritten elements."""
+    cfg = CONFIGS[idx]
+    inp = make_inputs(cfg)
+    note(f"measured layer {cfg.name} (table-selected config)")
+    gpu = run(cfg, inp)
+    assert not np.isnan(gpu).any()
+    if idx <= 1:
+        assert_close(gpu, ref_full(cfg, inp), cfg.name)
+    else:
+        rows = sample_rows(cfg, 3000, seed=idx)
+        assert_close(gpu.reshape(-1, cfg.C)[rows], ref_rows(cfg, inp, rows), cfg.name)
+    cid, cached = cb.conv2d_dgrad_query_config(cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S, cfg.stride,
+                                               cfg.pad, cfg.epilogue)
+    assert cached
+
+
+@pytest.mark.parametrize("idx", range(2, len(CONFIGS)), ids=[c.name for c in CONFIGS[2:]])
+def test_measured_layer_every_config(idx):
+    cfg = CONFIGS[idx]
+    inp = make_inputs(cfg)
+    rows = sample_rows(cfg, 600, seed=100 + idx)
+    ref = ref_rows(cfg, inp, rows)
+    for cid in range(cb.conv2d_dgrad_num_configs()):
+        note(f"measured layer {cfg.name} config {cid}")
+        gpu = run(cfg, inp, config_id=cid)
+        assert not np.isnan(gpu).any()
+        assert_close(gpu.reshape(-1, cfg.C)[rows], ref, f"{cfg.name} config {cid}")
+
+
+def test_downsample_zero_pattern():
+    """1x1 stride 2: three of the four lattices are exact zeros."""
+    cfg = CONFIGS[3]
+    inp = make_inputs(cfg)
+    note("zero pattern, 1x1 stride 2 at full size")
+    gpu = run(cfg, inp)
+    assert np.all(gpu[:, 1::2, :, :] == 0) and np.all(gpu[:, :, 1::2, :] == 0)
+    assert np.count_nonzero(gpu[:, ::2, ::2, :]) > 0.99 * gpu[:, ::2, ::2, :].size
+
+
+# ---------------------------------------------------------------- bit-exact cases
+
+def _bits_equal(gpu, ref16):
+    g = np.asarray(gpu, dtype=np.float16)
+    assert not np.isnan(g).any()
+    # +0 and -0 compare equal; everything else must be the same fp16 value
+    assert np.array_equal(g, ref16), f"{np.sum(g != ref16)} elements differ"
+
+
+@pytest.mark.parametrize("shape", [(2, 12, 12, 64, 64, 3, 3, 1, 1), (2, 13, 14, 72, 64, 3, 3, 2, 1),
+                                   (1, 9, 9, 16, 136, 1, 1, 2, 0), (1, 10, 11, 24, 40, 5, 3, 3, 2)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_integer_inputs_bit_exact(shape):
+    """Integer dy, w in [-8, 8]: every partial sum is an exact fp32 integer,
+    and sums above 2048 exercise fp16 round-to-nearest-even."""
+    cfg = _cfg(shape)
+    inp = integer_inputs(cfg, lo=-8, hi=8, seed=21)
+    ref16 = oracle.round_to_half(ref_full(cfg, inp))
+    for cid in range(cb.conv2d_dgrad_num_configs()):
+        note(f"integer bit-exact {shape} config {cid}")
+        _bits_equal(run(cfg, inp, config_id=cid), ref16)
+
+
+def test_fp16_rounding_is_nearest_even():
+    """1x1, stride 1, w = 1: dx = dy[...,0] + dy[...,1] = 2048 + {1,3,5,7}.
+    fp16 spacing is 2 there, so 2049/2051/2053/2055 are exact ties that
+    round-to-nearest-even sends to 2048/2052/2052/2056 (truncation would
+    give 2048/2050/2052/2054)."""
+    cfg = _cfg((1, 8, 8, 16, 8, 1, 1, 1, 0))
+    rng = np.random.Generator(np.random.PCG64(24))
+    dy = np.zeros((1, 8, 8, 8), np.float16)
+    dy[..., 0] = 2048
+    dy[..., 1] = rng.choice([1, 3, 5, 7], size=(1, 8, 8))
+    w = np.zeros((8, 1, 1, 16), np.float16)
+    w[0:2] = 1
+    inp = {"dy": dy, "w": w, "z": None}
+    note("fp16 rounding ties")
+    gpu = run(cfg, inp)
+    want = {2049: 2048, 2051: 2052, 2053: 2052, 2055: 2056}
+    exact = 2048 + dy[..., 1].astype(np.float64)
+    for v, r in want.items():
+        sel = exact[0] == v
+        assert np.all(gpu[0][sel] == r), v
+    _bits_equal(gpu, oracle.round_to_half(ref_full(cfg, inp)))
+
+
+@pytest.mark.parametrize("epi", [EPI_DRELU, EPI_DHARDSWISH])
+def test_epilogue_ties_bit_exact(epi):
+    """z at the kinks and zero crossings (-4, -3, -1.5, 0, 1.5, 3, 4), where
+    g is exact in fp32: the fused result is bit-exact."""
+    cfg = _cfg((2, 14, 14, 64, 32, 3, 3, 1, 1), epi)
+    inp = integer_inputs(cfg, lo=-2, hi=2, seed=22)
+    ref16 = oracle.round_to_half(ref_full(cfg, inp))
+    note(f"epilogue ties epi {epi}")
+    _bits_equal(run(cfg, inp), ref16)
+
+
+@pytest.mark.parametrize("stride,pad", [(2, 1), (3, 1), (2, 0)])
+def test_one_hot_footprints(stride, pad):
+    """One nonzero dy element lands exactly on the taps p*s - pad + r."""
+    cfg = _cfg((2, 11, 10, 16, 8, 3, 3, stride, pad))
+    base = integer_inputs(cfg, lo=-4, hi=4, seed=23)
+    positions = [(0, 0, 0, 0), (1, cfg.P - 1, cfg.Q - 1, 7), (0, cfg.P // 2, 1, 3), (1, 0, cfg.Q - 1, 5)]
+    for (n, p, q, k) in positions:
+        inp = {"dy": one_hot_dy(cfg, n, p, q, k), "w": base["w"], "z": None}
+        ref = ref_full(cfg, inp)
+        note(f"one-hot stride {stride} pad {pad} at {(n, p, q, k)}")
+        gpu = run(cfg, inp)
+        _bits_equal(gpu, oracle.round_to_half(ref))
+        support = {(int(a), int(b)) for a, b in zip(*np.nonzero(np.any(gpu[n] != 0, axis=-1)))}
+        want = {(p * stride - pad + r, q * stride - pad + t) for r in range(3) for t in range(3)
+                if 0 <= p * stride - pad + r < cfg.H and 0 <= q * stride - pad + t < cfg.W}
+        assert support <= want
+        assert np.all(gpu[1 - n] == 0)
+
+
+# ---------------------------------------------------------------- behaviour
+
+def test_deterministic():
+    cfg = CONFIGS[2]
+    inp = make_inputs(cfg)
+    note("determinism, strided 3x3 at full size")
+    a = run(cfg, inp)
+    b = run(cfg, inp)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_non_default_stream():
+    import torch
+    cfg = _cfg((2, 15, 13, 136, 72, 3, 3, 2, 1), EPI_DHARDSWISH)
+    inp = make_inputs(cfg)
+    s = torch.cuda.Stream()
+    note("non-default stream")
+    assert_close(run(cfg, inp, stream=s), ref_full(cfg, inp), "side stream")
+
+
+def test_autotune_off_uses_heuristic():
+    cfg = _cfg((1, 16, 16, 64, 64, 3, 3, 1, 1))
+    inp = make_inputs(cfg)
+    prev = cb.conv2d_dgrad_set_autotune(False)
+    try:
+        want, cached = cb.conv2d_dgrad_query_config(cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
+                                                    cfg.stride, cfg.pad)
+        assert not cached
+        note("autotune off")
+        assert_close(run(cfg, inp), ref_full(cfg, inp), "heuristic")
+        got, cached = cb.conv2d_dgrad_query_config(cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
+                                                   cfg.stride, cfg.pad)
+        assert cached and got == want
+    finally:
+        cb.conv2d_dgrad_set_autotune(prev)
