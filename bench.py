@@ -71,7 +71,7 @@ def measured_traffic(kernel_key):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def cpu_baseline(inputs, fraction, seed=99):
+def cpu_baseline(inputs, fraction, suite, seed=99):
     """The oracle, untuned, on a seeded `fraction` of each layer's output
     pixels; the full-suite time is extrapolated by 1/fraction per layer."""
     import oracle
@@ -79,7 +79,7 @@ def cpu_baseline(inputs, fraction, seed=99):
     threads = oracle.max_threads(lib)
     total_t = 0.0
     rows_done = 0
-    for idx in SUITE:
+    for idx in suite:
         cfg = CONFIGS[idx]
         npix = cfg.N * cfg.H * cfg.W
         k = max(1, int(round(npix * fraction)))
@@ -93,7 +93,7 @@ def cpu_baseline(inputs, fraction, seed=99):
         total_t += dt * npix / k
         rows_done += k
         log(f"[cpu] {cfg.name}: {k} of {npix} pixels in {dt:.2f} s")
-    flops = sum(CONFIGS[i].useful_flops() for i in SUITE)
+    flops = sum(CONFIGS[i].useful_flops() for i in suite)
     return {"value": flops / total_t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"seeded {fraction:.0%} of the output pixels of each suite layer "
                       f"({rows_done} pixel rows, all channels, fp64); full-suite time extrapolated "
@@ -105,8 +105,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-fraction", type=float, default=0.5,
+    ap.add_argument("--cpu-fraction", type=float, default=1.0,
                     help="share of each layer's pixels the oracle computes for cpu_baseline (0 skips it)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated layer names: time only these (for profiler runs)")
+    ap.add_argument("--copy-calibrate-mb", type=float, default=0.0,
+                    help="run only a plain device-to-device copy of this many MB, 10 times "
+                         "(reference for the HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -124,9 +129,27 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.copy_calibrate_mb > 0:
+        n = int(args.copy_calibrate_mb * 1e6) // 2
+        src = torch.empty(n, dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "launches": 10}), flush=True)
+        return
+
+    suite = SUITE
+    if args.only:
+        names = set(args.only.split(","))
+        suite = [i for i in SUITE if CONFIGS[i].name in names]
+        if not suite:
+            print(f"--only matched no layer of {[CONFIGS[i].name for i in SUITE]}", file=sys.stderr)
+            sys.exit(2)
+
     # ---- inputs, resident in HBM before timing
     host_inputs, layers = {}, []
-    for idx in SUITE:
+    for idx in suite:
         cfg = CONFIGS[idx]
         inp = make_inputs(cfg)
         host_inputs[idx] = inp
@@ -192,7 +215,7 @@ def main():
 
     cpu = None
     if args.cpu_fraction > 0:
-        cpu = cpu_baseline(host_inputs, args.cpu_fraction)
+        cpu = cpu_baseline(host_inputs, args.cpu_fraction, suite)
 
     out = {
         "metric": METRIC,

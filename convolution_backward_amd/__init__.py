@@ -68,12 +68,20 @@ def _bind(lib):
 
 
 def get_lib():
-    """The loaded HIP library; raises if it has not been built."""
+    """The loaded HIP library; raises if it has not been built.
+
+    PyTorch carries its own HIP runtime (same soname as ROCm's). It is loaded
+    first so that this library binds to that one runtime instead of bringing
+    a second copy into the process."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m convolution_backward_amd.build` (hipcc, gfx950)")
+        try:
+            import torch  # noqa: F401  (loads the HIP runtime the tensors live in)
+        except ImportError:
+            pass
         _lib = _bind(ctypes.CDLL(LIB_PATH))
     return _lib
 
