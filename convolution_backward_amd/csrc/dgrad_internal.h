@@ -31,6 +31,9 @@ struct KernelArgs {
     const uint16_t* w;
     uint16_t* dx;
     const uint16_t* z;
+    uint32_t dy_bytes;   // buffer sizes for the hardware range check
+    uint32_t w_bytes;
+    uint32_t dx_bytes;   // also the size of z
     int H, W, C, K, R, S, P, Q;
     int stride;
     int epi;

@@ -66,7 +66,7 @@ extern "C" {
                                            pointer not 16-byte aligned, dx overlapping
                                            an input, bad config id */
 #define CONV2D_DGRAD_UNSUPPORTED 2      /* C or K not a multiple of 8, a tensor of
-                                           2^31 elements or more, stride > 16 */
+                                           2^30 elements or more, stride > 16 */
 #define CONV2D_DGRAD_HIP_ERROR 3        /* a HIP runtime call or launch failed */
 
 /* epilogue kinds */
@@ -83,7 +83,7 @@ extern "C" {
  * P and Q are derived from H, W, R, S, stride and pad as above (several H give
  * the same P under stride > 1, which is why H and W are passed).
  * Constraints: C % 8 == 0, K % 8 == 0 (16-byte vectors along channels), all
- * pointers 16-byte aligned, every tensor below 2^31 elements.
+ * pointers 16-byte aligned, every tensor below 2^30 elements (2 GiB).
  */
 int conv2d_dgrad_nhwc(const void* dy, const void* w, void* dx,
                       int N, int H, int W, int C, int K, int R, int S,
