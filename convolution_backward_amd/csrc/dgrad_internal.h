@@ -21,6 +21,7 @@ struct PhaseArg {
     int r0, t0;          // first taps
     int dr0, dt0;        // dy offsets of the first taps
     int M;               // N*Hp*Wp
+    int tiles_m;         // ceil(M / BM)
     int tile_begin;      // first tile id of this phase in the launch
     FastDiv div_hw;      // division by Hp*Wp
     FastDiv div_w;       // division by Wp
@@ -38,8 +39,11 @@ struct KernelArgs {
     int stride;
     int epi;
     int tiles_n;         // tiles along C
-    int total_tiles;     // grid size
-    int group;           // consecutive tiles kept on one XCD
+    int total_tiles;     // tiles over all phases of the launch
+    int grid;            // resident workgroups walking them (<= total_tiles)
+    int order;           // 0: channel tiles of a pixel block consecutive; 1: pixel blocks of a channel tile
+    int xcd_mode;        // 0: rotating groups of `group` tiles per XCD; 1: contiguous eighths
+    int group;           // consecutive tiles kept on one XCD (mode 0)
     int nphases;
     PhaseArg ph[kMaxPhasesPerLaunch];
 };
@@ -56,5 +60,6 @@ struct TileConfig {
 int num_tile_configs();
 const TileConfig& tile_config(int id);
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);
+int blocks_per_cu(int id);   // resident workgroups per CU (current device)
 
 }  // namespace cbw
