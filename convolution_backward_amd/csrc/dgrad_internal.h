@@ -13,7 +13,7 @@ namespace cbw {
 // Phases per launch; strides above 4 are split over several launches.
 constexpr int kMaxPhasesPerLaunch = 16;
 
-// One stride phase as the kernel sees it (see dgrad_plan.h for the algebra).
+// One stride phase with taps, as the kernel sees it (see dgrad_plan.h for the algebra).
 struct PhaseArg {
     int ph, pw;          // lattice offsets
     int Wp;              // lattice width
@@ -27,6 +27,26 @@ struct PhaseArg {
     FastDiv div_w;       // division by Wp
 };
 
+// One zero phase (no tap reaches its lattice): its M*C/8 16-byte vectors of
+// zeros form the range [vbegin, vbegin + M*C/8) of the launch's zero-vector
+// list. Each phase's range is padded to a whole number of stripes (one
+// vector per thread of the workgroup), so a stripe never straddles phases.
+struct ZeroPhaseArg {
+    int ph, pw;          // lattice offsets
+    int Wp;              // lattice width
+    int M;               // N*Hp*Wp
+    uint32_t vbegin;     // first vector of this phase in the list (a stripe boundary)
+    FastDiv div_hw;      // division by Hp*Wp
+    FastDiv div_w;       // division by Wp
+};
+
+// Work of one launch, walked by a persistent grid:
+//   items [0, gemm_tiles)            GEMM tiles of the phases with taps; tile t
+//                                    also stores zero stripes [t*zt, (t+1)*zt)
+//                                    of the zero list, zps stripes with each of
+//                                    its slice requests
+//   items [gemm_tiles, total_tiles)  chunks of 8 zero stripes each, starting
+//                                    at stripe zabsorbed
 struct KernelArgs {
     const uint16_t* dy;
     const uint16_t* w;
@@ -39,14 +59,28 @@ struct KernelArgs {
     int stride;
     int epi;
     int tiles_n;         // tiles along C
-    int total_tiles;     // tiles over all phases of the launch
+    int gemm_tiles;      // GEMM tiles over all phases with taps
+    int total_tiles;     // GEMM tiles + zero chunks
     int grid;            // resident workgroups walking them (<= total_tiles)
     int order;           // 0: channel tiles of a pixel block consecutive; 1: pixel blocks of a channel tile
     int xcd_mode;        // 0: rotating groups of `group` tiles per XCD; 1: contiguous eighths
     int group;           // consecutive tiles kept on one XCD (mode 0)
     int nphases;
     PhaseArg ph[kMaxPhasesPerLaunch];
+    // zero phases
+    int nzphases;
+    uint32_t zstripes;   // stripes in the zero list (padded)
+    uint32_t zabsorbed;  // stripes stored by GEMM tiles (min(gemm_tiles * zt, zstripes))
+    int zps;             // zero stripes per slice request: 0..kMaxZeroPerSlice
+    int zt;              // zero stripes per GEMM tile (<= zps * fewest slices of a tile)
+    FastDiv div_c8;      // division by C/8
+    ZeroPhaseArg zph[kMaxPhasesPerLaunch];
 };
+
+// Zero stripes a slice request may carry (each is one 16-byte store per thread).
+constexpr int kMaxZeroPerSlice = 4;
+// Zero stripes per standalone chunk.
+constexpr int kZeroChunkStripes = 8;
 
 struct TileConfig {
     int BM;              // dx pixels per tile (GEMM rows)
@@ -61,5 +95,7 @@ int num_tile_configs();
 const TileConfig& tile_config(int id);
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);
 int blocks_per_cu(int id);   // resident workgroups per CU (current device)
+int kernel_private_bytes(int id);   // scratch bytes per lane of a config's kernel (-1: unknown)
+inline int threads_per_block(const TileConfig& tc) { return 64 * tc.WM * tc.WN; }
 
 }  // namespace cbw

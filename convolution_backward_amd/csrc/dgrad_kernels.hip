@@ -106,6 +106,29 @@ __device__ inline void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI] (the count is an
+// immediate field): a binary search over scalar branches.
+template <int LO, int HI>
+__device__ inline void wait_vmcnt_range(uint32_t n)
+{
+    if constexpr (LO == HI) {
+        wait_vmcnt<LO>();
+    } else {
+        constexpr int MID = (LO + HI) / 2;
+        if (n <= (uint32_t)MID)
+            wait_vmcnt_range<LO, MID>(n);
+        else
+            wait_vmcnt_range<MID + 1, HI>(n);
+    }
+}
+
+// Wait until at most n vector-memory operations of this wave are
+// outstanding (n above the counter's range waits for 63).
+__device__ inline void wait_vmcnt_at_most(uint32_t n)
+{
+    wait_vmcnt_range<0, 63>(n < 63u ? n : 63u);
+}
+
 __device__ inline int dy_swizzle(int row)
 {
     return (row >> 1) & 7;
@@ -142,13 +165,19 @@ __device__ inline int xcd_remap(int b, int total, int g, int mode)
 // g(z) for the fused epilogues, evaluated in fp32 without branches.
 // relu'(z) = [z > 0]; hardswish'(z) = 0 below -3, z/3 + 1/2 on the closed
 // interval [-3, 3], 1 above 3 (the division is correctly rounded).
-__device__ inline float epilogue_factor(int epi, float z)
+template <int E>
+__device__ inline float epilogue_factor(float z)
 {
-    const float relu = z > 0.0f ? 1.0f : 0.0f;
+    if constexpr (E == kEpiDRelu)
+        return z > 0.0f ? 1.0f : 0.0f;
     const float mid = z / 3.0f + 0.5f;
-    const float hsw = z < -3.0f ? 0.0f : (z > 3.0f ? 1.0f : mid);
-    return epi == kEpiDRelu ? relu : (epi == kEpiDHardswish ? hsw : 1.0f);
+    return z < -3.0f ? 0.0f : (z > 3.0f ? 1.0f : mid);
 }
+
+template <int E>
+struct EpiTag {
+    static constexpr int value = E;
+};
 
 template <int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
@@ -170,7 +199,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole 1 KiB blocks per wave");
     static_assert(BN % 64 == 0, "filter rows of at least 8 chunks");
     static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS budget");
-    static_assert(2 * LD < 64, "vmcnt range");
+    static_assert(LD + 2 * kMaxZeroPerSlice < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];
     const uint32_t lds_u32 = (uint32_t)(uintptr_t)((lds_char*)lds);
@@ -197,6 +226,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     struct Tile {
         int pi, m0, c0, niter;
     };
+    // GEMM tile `tile` (< gemm_tiles): its phase, first lattice row, first channel, slices.
     auto decode = [&](int tile) -> Tile {
         int pi = 0;
         for (int i = 1; i < a.nphases; ++i)
@@ -225,6 +255,31 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         return pix * (uint32_t)C;
     };
 
+    // Zero stripe `stripe` (uniform): vectors stripe*NT .. stripe*NT+NT-1 of the
+    // zero list, one 16-byte store of zeros per thread. A stripe lies in one
+    // zero phase (ranges are stripe-aligned); padding vectors past the phase's
+    // M*C/8 and stripes past the list are dropped by the range check.
+    auto zero_stripe = [&](uint32_t stripe) {
+        const uint32_t vb = stripe * (uint32_t)NT;
+        int zp = 0;
+        for (int i = 1; i < a.nzphases; ++i)
+            if (vb >= a.zph[i].vbegin)
+                zp = i;
+        const ZeroPhaseArg& zph = a.zph[zp];
+        const uint32_t u = vb - zph.vbegin + (uint32_t)tid;
+        const uint32_t m = fastdiv(u, a.div_c8);
+        const uint32_t c = (u - m * a.div_c8.d) * 8u;
+        const uint32_t n = fastdiv(m, zph.div_hw);
+        const uint32_t rem = m - n * zph.div_hw.d;
+        const uint32_t i = fastdiv(rem, zph.div_w);
+        const uint32_t j = rem - i * (uint32_t)zph.Wp;
+        const uint32_t pix = (n * (uint32_t)a.H + (uint32_t)zph.ph + (uint32_t)s * i) * (uint32_t)a.W
+                             + (uint32_t)zph.pw + (uint32_t)s * j;
+        const uint32_t bad = (uint32_t)(m >= (uint32_t)zph.M) | (uint32_t)(stripe >= a.zstripes);
+        const u32x4 zero{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_raw_buffer_store_b128(zero, dx_rsrc, out_of_range_if(bad, (pix * (uint32_t)C + c) * 2u), 0, 0);
+    };
+
     // ---- request side: the stream of slices of this workgroup's tiles (zero
     // tiles have none), running up to two slices ahead of the matrix cores.
     // DMA block b = jn*NW + wave of a dy slice covers tile rows 8b..8b+7; lane l
@@ -246,24 +301,32 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     uint32_t a_off[A_INSTR];   // element offset of dy[n, i, j, chunk*8], modulo 2^32: a
     int a_i[A_INSTR];          // lattice row i may exceed P, but every offset that is
     int a_j[A_INSTR];          // loaded (0 <= i+dr < P, 0 <= j+dt < Q) is exact
-    int rq_round = 0, rq_left = 0, rq_pi = 0, rq_c0 = 0;
+    int rq_round = 0, rq_left = 0, rq_pi = 0, rq_c0 = 0, rq_tile = 0, rq_niter = 0;
     int ar = 0, at = 0, k0 = 0;
+    // Vector-memory operations this wave has issued (wave-uniform), and the
+    // count just after the last load of the slice held by each LDS stage.
+    // The hardware completes them in issue order, so slice x has landed once
+    // at most ops - last_load[x's stage] operations are outstanding.
+    // (Three scalars, not an array, so nothing is ever spilled to scratch
+    // memory: a scratch access would be an uncounted memory operation.)
+    uint32_t ops = 0;
+    uint32_t last_load0 = 0, last_load1 = 0, last_load2 = 0;
     // the slice being requested (set by prepare_next)
-    int q_dr = 0, q_dt = 0, q_wtap = 0;
+    int q_dr = 0, q_dt = 0, q_wtap = 0, rq_buf = 0;
     uint32_t q_tapoff = 0, q_base = 0;
     // Pick the next slice of the stream; false when the stream is exhausted.
     auto prepare_next = [&](int buf) -> bool {
         while (rq_left == 0) {  // move to the next tile that has slices
             const int tile = rq_round * G + slot;
-            if (tile >= a.total_tiles)
+            if (tile >= a.gemm_tiles)
                 return false;
             ++rq_round;
             const Tile t = decode(tile);
-            if (t.niter == 0)
-                continue;
             rq_pi = t.pi;
             rq_c0 = t.c0;
             rq_left = t.niter;
+            rq_niter = t.niter;
+            rq_tile = tile;
             ar = at = k0 = 0;
             const PhaseArg& ph = a.ph[t.pi];
 #pragma unroll
@@ -284,6 +347,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         q_tapoff = (uint32_t)(q_dr * a.Q + q_dt) * (uint32_t)K + (uint32_t)k0;
         q_wtap = ((ph.r0 + ar * s) * a.S + (ph.t0 + at * s)) * C;
         q_base = lds_u32 + (uint32_t)(buf * STAGE);
+        rq_buf = buf;
         return true;
     };
     // Issue part `part` (of 4) of the prepared slice's direct-to-LDS loads:
@@ -310,6 +374,23 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             }
         }
     };
+    // The zero stripes that ride with the prepared slice: slice number si of
+    // GEMM tile t stores stripes t*zt + si*zps + j (j < zps) of its share.
+    // Exactly zps stores per request, so the waits below can count them;
+    // those outside the tile's share are dropped by the range check.
+    auto issue_zero = [&]() {
+        ops += LD;              // this request's loads are all issued
+        last_load0 = rq_buf == 0 ? ops : last_load0;   // selects, not branches
+        last_load1 = rq_buf == 1 ? ops : last_load1;
+        last_load2 = rq_buf == 2 ? ops : last_load2;
+        ops += (uint32_t)a.zps;
+        const int si = rq_niter - rq_left;
+        for (int jz = 0; jz < a.zps; ++jz) {
+            const int idx = si * a.zps + jz;
+            const uint32_t stripe = (uint32_t)rq_tile * (uint32_t)a.zt + (uint32_t)idx;
+            zero_stripe(idx < a.zt && stripe < a.zabsorbed ? stripe : 0xffffffffu);
+        }
+    };
     // Advance the cursor past the issued slice. Taps innermost: consecutive
     // slices re-read the same dy rows (shifted by one tap), so the repeats hit in L2.
     auto finish_request = [&]() {
@@ -328,6 +409,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             return false;
         for (int part = 0; part < 4; ++part)
             issue_part(part);
+        issue_zero();
         finish_request();
         return true;
     };
@@ -392,37 +474,117 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         if (issue)
             issue_part(2);
         mfma_step(af0, bf0);
-        if (issue)
+        if (issue) {
             issue_part(3);
+            issue_zero();
+        }
         mfma_step(af1, bf1);
     };
 
-    // ---- the walk. R slices requested, C computed; slice x lives in LDS
-    // stage x % 3 (rotating counters rbuf, cbuf).
-    int R = 0, C_ = 0, rbuf = 0, cbuf = 0;
-    if (request_next(rbuf)) { ++R; rbuf = 1; }
-    if (request_next(rbuf)) { ++R; rbuf = 2; }
+    // ---- epilogue. The lane holds channels 8*gq + 4*(lane/32) .. +3 of
+    // block fn, pixel lane%32 of pixel group fm. The fused kinds load z in
+    // that layout (every load issued before the first use) and scale by g(z)
+    // in fp32; each value is rounded once to fp16. The fp16 results then pass
+    // through the LDS stage of the slice just computed (no request targets it
+    // until the next slice's barrier): each wave writes a block of 32 pixels x
+    // TN channels and reads it back as whole 16-byte chunks, so that one store
+    // instruction covers 64/CH pixels x TN*2 contiguous bytes instead of 32
+    // scattered 16-byte pieces. Chunk q of staged row p sits at position
+    // q ^ ((p >> 1) % CH).
+    constexpr int CH = TN / 8;            // 16-byte chunks per staged pixel row
+    constexpr int EROW = TN * 2;          // bytes per staged pixel row
+    constexpr int EBLK = 32 * EROW;       // bytes per wave per pixel group
+    constexpr int PPI = 64 / CH;          // pixels per store instruction
+    constexpr int EST = 32 / PPI;         // store instructions per pixel group
+    static_assert(NW * EBLK <= STAGE, "the staging blocks fit in one stage");
+    static_assert(CH >= 2 && CH <= 64 && 64 % CH == 0, "whole pixel rows per store");
+    const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(a.epi != kEpiNone ? a.z : a.dx, a.dx_bytes);
+    auto epilogue = [&](auto tag, const Tile& t, const PhaseArg& ph, int stage) {
+        constexpr int E = decltype(tag)::value;
+        const int cw = t.c0 + wn * TN;    // first channel of this wave's block
+        u32x2 zr[FM][FN][4];
+        if constexpr (E != kEpiNone) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int m = t.m0 + wm * TM + fm * 32 + (lane & 31);
+                const uint32_t pix = pixel_offset(ph, m);
+                const uint32_t m_bad = (uint32_t)(m >= ph.M);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int c = cw + fn * 32 + 8 * gq + 4 * (lane >> 5);
+                        zr[fm][fn][gq] = __builtin_amdgcn_raw_buffer_load_b64(
+                            z_rsrc, out_of_range_if(m_bad | (uint32_t)(c >= C), (pix + (uint32_t)c) * 2u), 0, 0);
+                    }
+            }
+        }
+        lds_char* blk = (lds_char*)lds + stage * STAGE + wave * EBLK;
+        __syncthreads();   // every wave is done reading the stage's operands
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int pw = lane & 31;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    float v0 = acc[fn][fm][4 * gq + 0];
+                    float v1 = acc[fn][fm][4 * gq + 1];
+                    float v2 = acc[fn][fm][4 * gq + 2];
+                    float v3 = acc[fn][fm][4 * gq + 3];
+                    if constexpr (E != kEpiNone) {
+                        const half4_t zz = __builtin_bit_cast(half4_t, zr[fm][fn][gq]);
+                        v0 *= epilogue_factor<E>((float)zz[0]);
+                        v1 *= epilogue_factor<E>((float)zz[1]);
+                        v2 *= epilogue_factor<E>((float)zz[2]);
+                        v3 *= epilogue_factor<E>((float)zz[3]);
+                    }
+                    const half4_t o{(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+                    const int q = fn * 4 + gq;
+                    *(__attribute__((address_space(3))) u32x2*)(blk + pw * EROW + ((q ^ ((pw >> 1) % CH)) * 16) + (lane >> 5) * 8) =
+                        __builtin_bit_cast(u32x2, o);
+                }
+            }
+            // read back whole chunks: instruction e covers pixels e*PPI .. e*PPI+PPI-1
+#pragma unroll
+            for (int e = 0; e < EST; ++e) {
+                const int pr = e * PPI + lane / CH;
+                const int q = lane % CH;
+                const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(blk + pr * EROW + ((q ^ ((pr >> 1) % CH)) * 16));
+                const int m = t.m0 + wm * TM + fm * 32 + pr;
+                const int c = cw + q * 8;
+                const uint32_t bad = (uint32_t)(m >= ph.M) | (uint32_t)(c >= C);
+                __builtin_amdgcn_raw_buffer_store_b128(v, dx_rsrc, out_of_range_if(bad, (pixel_offset(ph, m) + (uint32_t)c) * 2u), 0, 0);
+            }
+        }
+    };
+    // vector-memory operations of one epilogue
+    constexpr uint32_t kEpiStores = FM * EST;
+    constexpr uint32_t kEpiZLoads = FM * FN * 4;
+
+    // ---- the walk. The k-th slice of the stream lives in LDS stage k % 3:
+    // rbuf is the stage of the next request, cbuf that of the next slice to
+    // compute; requests run two slices ahead.
+    int rbuf = 0, cbuf = 0;
+    if (request_next(rbuf))
+        rbuf = 1;
+    if (request_next(rbuf))
+        rbuf = 2;
     const int epi = a.epi;
-    const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(epi != kEpiNone ? a.z : a.dx, a.dx_bytes);
     for (int round = 0;; ++round) {
         const int tile = round * G + slot;
         if (tile >= a.total_tiles)
             break;
-        const Tile t = decode(tile);
-        const PhaseArg& ph = a.ph[t.pi];
-
-        if (t.niter == 0) {  // zero phase: no tap reaches this lattice; dx is exactly 0 there
-            constexpr int ZV = BN / 8;  // 16-byte vectors per pixel row of the tile
-            const u32x4 zero{0u, 0u, 0u, 0u};
-            for (int u = tid; u < BM * ZV; u += NT) {
-                const int row = u / ZV;
-                const int c = t.c0 + (u - row * ZV) * 8;
-                const int m = t.m0 + row;
-                const uint32_t bad = (uint32_t)(m >= ph.M) | (uint32_t)(c >= C);
-                __builtin_amdgcn_raw_buffer_store_b128(zero, dx_rsrc, out_of_range_if(bad, (pixel_offset(ph, m) + (uint32_t)c) * 2u), 0, 0);
-            }
+        if (tile >= a.gemm_tiles) {   // a chunk of zero stripes (no request is in flight any more)
+            const uint32_t first = a.zabsorbed + (uint32_t)(tile - a.gemm_tiles) * kZeroChunkStripes;
+#pragma unroll
+            for (int u = 0; u < kZeroChunkStripes; ++u)
+                zero_stripe(first + u);
+            ops += kZeroChunkStripes;
             continue;
         }
+        const Tile t = decode(tile);
+        const PhaseArg& ph = a.ph[t.pi];
 
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
@@ -432,53 +594,29 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                 for (int e = 0; e < 16; ++e)
                     acc[fn][fm][e] = 0.0f;
         for (int it = 0; it < t.niter; ++it) {
-            // Slice C_ must have landed; slice C_+1 (if requested) may still fly.
-            // (Stores issued since only make these waits stricter.)
-            if (R - C_ >= 2)
-                wait_vmcnt<LD>();
-            else
-                wait_vmcnt<0>();
-            __syncthreads();     // every wave's part of slice C_ is in LDS, and every
+            // This slice must have landed; whatever was issued after its last
+            // load (later requests, zero stores, the previous tile's
+            // epilogue) may still be in flight.
+            wait_vmcnt_at_most(ops - (cbuf == 0 ? last_load0 : (cbuf == 1 ? last_load1 : last_load2)));
+            __syncthreads();     // every wave's part of the slice is in LDS, and every
                                  // wave is done with the stage the next request reuses
             const bool more = prepare_next(rbuf);
             compute(cbuf, more);
             if (more) {
                 finish_request();
-                ++R;
                 rbuf = rbuf == 2 ? 0 : rbuf + 1;
             }
-            ++C_;
             cbuf = cbuf == 2 ? 0 : cbuf + 1;
         }
 
-        // ---- epilogue: lane holds channels c..c+3 of pixel m per register
-        // group; out-of-range lanes store to an offset the hardware drops.
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int m = t.m0 + wm * TM + fm * 32 + (lane & 31);
-            const uint32_t pix = pixel_offset(ph, m);
-            const uint32_t m_bad = (uint32_t)(m >= ph.M);
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int c = t.c0 + wn * TN + fn * 32 + 8 * gq + 4 * (lane >> 5);
-                    const uint32_t off = out_of_range_if(m_bad | (uint32_t)(c >= C), (pix + (uint32_t)c) * 2u);
-                    float v0 = acc[fn][fm][4 * gq + 0];
-                    float v1 = acc[fn][fm][4 * gq + 1];
-                    float v2 = acc[fn][fm][4 * gq + 2];
-                    float v3 = acc[fn][fm][4 * gq + 3];
-                    if (epi != kEpiNone) {
-                        const half4_t zz = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(z_rsrc, off, 0, 0));
-                        v0 *= epilogue_factor(epi, (float)zz[0]);
-                        v1 *= epilogue_factor(epi, (float)zz[1]);
-                        v2 *= epilogue_factor(epi, (float)zz[2]);
-                        v3 *= epilogue_factor(epi, (float)zz[3]);
-                    }
-                    const half4_t o{(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), dx_rsrc, off, 0, 0);
-                }
-            }
+        // ---- epilogue (one specialisation per kind; the kind is uniform),
+        // staged through the stage of the slice just computed
+        ops += kEpiStores + (epi != kEpiNone ? kEpiZLoads : 0u);
+        const int sdone = cbuf == 0 ? 2 : cbuf - 1;
+        switch (epi) {
+        case kEpiDRelu: epilogue(EpiTag<kEpiDRelu>{}, t, ph, sdone); break;
+        case kEpiDHardswish: epilogue(EpiTag<kEpiDHardswish>{}, t, ph, sdone); break;
+        default: epilogue(EpiTag<kEpiNone>{}, t, ph, sdone); break;
         }
     }
 }
@@ -507,7 +645,6 @@ int resident(void)
 #define CBW_TILE_CONFIGS(X) \
     X(256, 128, 2, 2)       \
     X(128, 128, 2, 2)       \
-    X(128, 256, 2, 2)       \
     X(256, 64, 4, 1)        \
     X(128, 64, 2, 2)        \
     X(64, 64, 2, 2)         \
@@ -517,13 +654,29 @@ int resident(void)
 #define CBW_CONFIG_ENTRY(BM, BN, WM, WN) {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN, 3 * (BM + BN) * 64 * 2},
 const TileConfig kConfigs[] = {CBW_TILE_CONFIGS(CBW_CONFIG_ENTRY)};
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+static_assert(kNumConfigs <= 64, "the launcher keeps per-config state for at most 64 configs");
+
+// Private (scratch) bytes per lane of one configuration's kernel, or -1 if
+// the runtime cannot tell.
+template <int BM, int BN, int WM, int WN>
+int private_bytes(void)
+{
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN>)) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return (int)attr.localSizeBytes;
+}
 
 using LaunchFn = hipError_t (*)(const KernelArgs&, hipStream_t);
 using ResidentFn = int (*)(void);
 #define CBW_LAUNCH_ENTRY(BM, BN, WM, WN) &launch<BM, BN, WM, WN>,
 #define CBW_RESIDENT_ENTRY(BM, BN, WM, WN) &resident<BM, BN, WM, WN>,
+#define CBW_PRIVATE_ENTRY(BM, BN, WM, WN) &private_bytes<BM, BN, WM, WN>,
 const LaunchFn kLaunch[] = {CBW_TILE_CONFIGS(CBW_LAUNCH_ENTRY)};
 const ResidentFn kResident[] = {CBW_TILE_CONFIGS(CBW_RESIDENT_ENTRY)};
+const ResidentFn kPrivate[] = {CBW_TILE_CONFIGS(CBW_PRIVATE_ENTRY)};
 
 }  // namespace
 
@@ -534,6 +687,11 @@ const TileConfig& tile_config(int id) { return kConfigs[id]; }
 int blocks_per_cu(int id)
 {
     return (id >= 0 && id < kNumConfigs) ? kResident[id]() : 1;
+}
+
+int kernel_private_bytes(int id)
+{
+    return (id >= 0 && id < kNumConfigs) ? kPrivate[id]() : -1;
 }
 
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream)

@@ -16,7 +16,8 @@ from tests.gpu_util import assert_close, note, ref_full, ref_rows, run, sample_r
 pytestmark = pytest.mark.gpu
 
 # N, H, W, C, K, R, S, stride, pad: several tiles, ragged tails in M, C and K,
-# every stride-phase situation (zero phases, empty lattices, >16 phases).
+# every stride-phase situation (zero phases carried by GEMM tiles or left to
+# standalone chunks, empty lattices, >16 phases).
 SMALL = [
     (2, 15, 13, 136, 72, 3, 3, 1, 1),
     (2, 17, 16, 64, 128, 3, 3, 2, 1),
@@ -31,6 +32,8 @@ SMALL = [
     (1, 3, 3, 8, 8, 3, 3, 4, 2),
     (1, 33, 35, 8, 8, 3, 3, 16, 1),
     (4, 28, 28, 192, 320, 3, 3, 1, 1),
+    (2, 12, 12, 16, 8, 1, 1, 4, 0),
+    (2, 30, 30, 48, 136, 1, 1, 3, 0),
 ]
 
 
