@@ -71,7 +71,7 @@ struct KernelArgs {
     int nzphases;
     uint32_t zstripes;   // stripes in the zero list (padded)
     uint32_t zabsorbed;  // stripes stored by GEMM tiles (min(gemm_tiles * zt, zstripes))
-    int zps;             // zero stripes per slice request: 0..kMaxZeroPerSlice
+    int zps;             // zero stripes per slice request: 0 or kMaxZeroPerSlice
     int zt;              // zero stripes per GEMM tile (<= zps * fewest slices of a tile)
     FastDiv div_c8;      // division by C/8
     ZeroPhaseArg zph[kMaxPhasesPerLaunch];

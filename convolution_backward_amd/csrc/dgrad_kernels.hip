@@ -90,13 +90,33 @@ __device__ inline i32x4 raw_descriptor(const void* base, uint32_t bytes)
     return i32x4{(int)(uint32_t)p, (int)((p >> 32) & 0xffffu), (int)bytes, kRawBufferFlags};
 }
 
-// One 16-byte direct-to-LDS load per lane: LDS[lds_base + 16*lane] <- buffer[voffset].
-__device__ inline void dma16(i32x4 desc, uint32_t voffset, uint32_t lds_base)
+// One 16-byte direct-to-LDS load per lane: LDS[lds_base + 16*lane] <-
+// buffer[voffset + soffset] (soffset wave-uniform). An in-range lane has
+// voffset + soffset inside the buffer; an out-of-range lane has voffset =
+// 2^31 (and soffset < 2^31), outside the buffer however the hardware combines
+// the two offsets for its range check.
+__device__ inline void dma16(i32x4 desc, uint32_t voffset, uint32_t soffset, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    const int so = __builtin_amdgcn_readfirstlane((int)soffset);   // uniform by construction
+    const int lb = __builtin_amdgcn_readfirstlane((int)lds_base);
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "v"(voffset), "s"(desc), "s"(lds_base)
+                 : "v"(voffset), "s"(desc), "s"(so), "s"(lb)
                  : "memory", "m0");
+}
+
+// A wave-uniform 32-bit value kept in a scalar register: the compiler may
+// not re-derive it later from the kernel arguments (a scalar memory load,
+// whose wait would also drain the LDS reads in flight). The value is taken
+// from the first active lane, which is exact for a uniform value wherever the
+// compiler happened to hold it.
+template <typename T>
+__device__ inline T pin(T x)
+{
+    static_assert(sizeof(T) == 4, "32-bit values");
+    int v = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x));
+    asm volatile("" : "+s"(v));
+    return __builtin_bit_cast(T, v);
 }
 
 template <int N>
@@ -104,29 +124,6 @@ __device__ inline void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-// s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI] (the count is an
-// immediate field): a binary search over scalar branches.
-template <int LO, int HI>
-__device__ inline void wait_vmcnt_range(uint32_t n)
-{
-    if constexpr (LO == HI) {
-        wait_vmcnt<LO>();
-    } else {
-        constexpr int MID = (LO + HI) / 2;
-        if (n <= (uint32_t)MID)
-            wait_vmcnt_range<LO, MID>(n);
-        else
-            wait_vmcnt_range<MID + 1, HI>(n);
-    }
-}
-
-// Wait until at most n vector-memory operations of this wave are
-// outstanding (n above the counter's range waits for 63).
-__device__ inline void wait_vmcnt_at_most(uint32_t n)
-{
-    wait_vmcnt_range<0, 63>(n < 63u ? n : 63u);
 }
 
 __device__ inline int dy_swizzle(int row)
@@ -209,11 +206,17 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM;
     const int wn = wave / WM;
-    const int s = a.stride;
-    const int C = a.C;
-    const int K = a.K;
+    const int s = pin(a.stride);
+    const int C = pin(a.C);
+    const int K = pin(a.K);
+    const int P = pin(a.P);
+    const int Q = pin(a.Q);
     const int ksteps = (K + BK - 1) / BK;
-    const int RSC = a.R * a.S * C;
+    const int SC = pin(a.S * C);          // filter elements per tap row
+    const int RSC = pin(a.R * SC);        // filter elements per k
+    const uint32_t zps = pin((uint32_t)a.zps);
+    const uint32_t zt = pin((uint32_t)a.zt);
+    const uint32_t zabsorbed = pin(a.zabsorbed);
 
     const __amdgpu_buffer_rsrc_t dx_rsrc = make_rsrc(a.dx, a.dx_bytes);
     const i32x4 dy_desc = raw_descriptor(a.dy, a.dy_bytes);
@@ -258,35 +261,57 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     // Zero stripe `stripe` (uniform): vectors stripe*NT .. stripe*NT+NT-1 of the
     // zero list, one 16-byte store of zeros per thread. A stripe lies in one
     // zero phase (ranges are stripe-aligned); padding vectors past the phase's
-    // M*C/8 and stripes past the list are dropped by the range check.
-    auto zero_stripe = [&](uint32_t stripe) {
+    // M*C/8 and stripes past the list are dropped by the range check. The
+    // stripes a workgroup stores only increase, so the zero phase in use is a
+    // cursor that moves forward.
+    int zc = -1;                          // current zero phase
+    uint32_t zc_begin = 0, zc_next = 0;   // its first vector, and the next phase's
+    int zc_ph = 0, zc_pw = 0, zc_Wp = 0, zc_M = 0;
+    FastDiv zc_hw{1, 0, 0}, zc_w{1, 0, 0};
+    auto zero_stripe = [&](uint32_t stripe, bool valid) {
         const uint32_t vb = stripe * (uint32_t)NT;
-        int zp = 0;
-        for (int i = 1; i < a.nzphases; ++i)
-            if (vb >= a.zph[i].vbegin)
-                zp = i;
-        const ZeroPhaseArg& zph = a.zph[zp];
-        const uint32_t u = vb - zph.vbegin + (uint32_t)tid;
+        if (valid) {
+            while (vb >= zc_next) {       // rare: enter the next zero phase
+                ++zc;
+                const ZeroPhaseArg& z = a.zph[zc];
+                zc_begin = z.vbegin;
+                zc_next = zc + 1 < a.nzphases ? a.zph[zc + 1].vbegin : 0xffffffffu;
+                zc_ph = z.ph;
+                zc_pw = z.pw;
+                zc_Wp = z.Wp;
+                zc_M = z.M;
+                zc_hw = z.div_hw;
+                zc_w = z.div_w;
+            }
+        }
+        const uint32_t u = vb - zc_begin + (uint32_t)tid;
         const uint32_t m = fastdiv(u, a.div_c8);
         const uint32_t c = (u - m * a.div_c8.d) * 8u;
-        const uint32_t n = fastdiv(m, zph.div_hw);
-        const uint32_t rem = m - n * zph.div_hw.d;
-        const uint32_t i = fastdiv(rem, zph.div_w);
-        const uint32_t j = rem - i * (uint32_t)zph.Wp;
-        const uint32_t pix = (n * (uint32_t)a.H + (uint32_t)zph.ph + (uint32_t)s * i) * (uint32_t)a.W
-                             + (uint32_t)zph.pw + (uint32_t)s * j;
-        const uint32_t bad = (uint32_t)(m >= (uint32_t)zph.M) | (uint32_t)(stripe >= a.zstripes);
+        const uint32_t n = fastdiv(m, zc_hw);
+        const uint32_t rem = m - n * zc_hw.d;
+        const uint32_t i = fastdiv(rem, zc_w);
+        const uint32_t j = rem - i * (uint32_t)zc_Wp;
+        const uint32_t pix = (n * (uint32_t)a.H + (uint32_t)zc_ph + (uint32_t)s * i) * (uint32_t)a.W
+                             + (uint32_t)zc_pw + (uint32_t)s * j;
+        const uint32_t bad = (uint32_t)!valid | (uint32_t)(m >= (uint32_t)zc_M);
         const u32x4 zero{0u, 0u, 0u, 0u};
         __builtin_amdgcn_raw_buffer_store_b128(zero, dx_rsrc, out_of_range_if(bad, (pix * (uint32_t)C + c) * 2u), 0, 0);
     };
 
-    // ---- request side: the stream of slices of this workgroup's tiles (zero
-    // tiles have none), running up to two slices ahead of the matrix cores.
+    // ---- request side: the stream of slices of this workgroup's GEMM tiles,
+    // running up to two slices ahead of the matrix cores. A tile's slices go
+    // tap by tap and, within a tap, over k in BK-wide steps. A lane's dy
+    // address then changes only at tap boundaries: for a whole tap it is a
+    // per-lane byte offset (or the out-of-range offset 2^31 for a padding tap
+    // or a dead row) plus the wave-uniform 2*k0, which goes into the load's
+    // scalar offset; a full-width slice needs no per-lane arithmetic at all.
+    // Only a ragged last k step (K not a multiple of BK) masks lanes further.
     // DMA block b = jn*NW + wave of a dy slice covers tile rows 8b..8b+7; lane l
     // fills row 8b + l/8 at chunk position l%8, holding logical chunk
     // (l%8) ^ dy_swizzle(row). Byte 16*l of block jn*NW + wave of a filter
     // slice is row k, position p, holding logical chunk p ^ 2*(k & 3).
     int a_k[A_INSTR], b_k[B_INSTR], b_c[B_INSTR];
+    uint32_t w_lane[B_INSTR];  // byte offset of the lane's filter element within a slice
 #pragma unroll
     for (int jn = 0; jn < A_INSTR; ++jn)
         a_k[jn] = ((lane & 7) ^ dy_swizzle((jn * NW + wave) * 8 + (lane >> 3))) * 8;
@@ -297,38 +322,40 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         const int pos = (byte % B_ROW) / 16;
         b_k[jn] = k;
         b_c[jn] = (pos ^ (2 * (k & 3))) * 8;
+        w_lane[jn] = (uint32_t)(k * RSC + b_c[jn]) * 2u;
     }
-    uint32_t a_off[A_INSTR];   // element offset of dy[n, i, j, chunk*8], modulo 2^32: a
+    uint32_t a_off[A_INSTR];   // byte offset of dy[n, i, j, chunk*8], modulo 2^32: a
     int a_i[A_INSTR];          // lattice row i may exceed P, but every offset that is
     int a_j[A_INSTR];          // loaded (0 <= i+dr < P, 0 <= j+dt < Q) is exact
-    int rq_round = 0, rq_left = 0, rq_pi = 0, rq_c0 = 0, rq_tile = 0, rq_niter = 0;
+    uint32_t dy_vo[A_INSTR];   // the lane's dy byte offset for the current tap and k step
+    uint32_t w_vt[B_INSTR];    // the lane's filter byte offset for the tile (2^31: channel past C)
+    uint32_t w_vo[B_INSTR];    // ... for the current k step
+    int rq_round = 0, rq_left = 0, rq_c0 = 0, rq_tile = 0, rq_niter = 0;
+    // taps of the tile being requested (scalar copies of its phase's fields)
+    int rq_dr0 = 0, rq_dt0 = 0, rq_nt = 1, rq_wt0 = 0;
     int ar = 0, at = 0, k0 = 0;
-    // Vector-memory operations this wave has issued (wave-uniform), and the
-    // count just after the last load of the slice held by each LDS stage.
-    // The hardware completes them in issue order, so slice x has landed once
-    // at most ops - last_load[x's stage] operations are outstanding.
-    // (Three scalars, not an array, so nothing is ever spilled to scratch
-    // memory: a scratch access would be an uncounted memory operation.)
-    uint32_t ops = 0;
-    uint32_t last_load0 = 0, last_load1 = 0, last_load2 = 0;
-    // the slice being requested (set by prepare_next)
-    int q_dr = 0, q_dt = 0, q_wtap = 0, rq_buf = 0;
-    uint32_t q_tapoff = 0, q_base = 0;
+    bool new_tap = true;       // the cursor entered a new tap: recompute the lanes' offsets
+    uint32_t q_wtap = 0;       // filter byte offset of the current tap (wave-uniform)
+    uint32_t q_base = 0;       // LDS address of the stage being filled
     // Pick the next slice of the stream; false when the stream is exhausted.
     auto prepare_next = [&](int buf) -> bool {
-        while (rq_left == 0) {  // move to the next tile that has slices
+        while (rq_left == 0) {  // move to the next tile
             const int tile = rq_round * G + slot;
             if (tile >= a.gemm_tiles)
                 return false;
             ++rq_round;
             const Tile t = decode(tile);
-            rq_pi = t.pi;
             rq_c0 = t.c0;
             rq_left = t.niter;
             rq_niter = t.niter;
             rq_tile = tile;
             ar = at = k0 = 0;
+            new_tap = true;
             const PhaseArg& ph = a.ph[t.pi];
+            rq_dr0 = pin(ph.dr0);
+            rq_dt0 = pin(ph.dt0);
+            rq_nt = pin(ph.nt);
+            rq_wt0 = pin(ph.r0 * SC + ph.t0 * C);
 #pragma unroll
             for (int jn = 0; jn < A_INSTR; ++jn) {
                 const int m = t.m0 + (jn * NW + wave) * 8 + (lane >> 3);
@@ -338,16 +365,36 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                 const uint32_t j = rem - i * (uint32_t)ph.Wp;
                 a_i[jn] = m < ph.M ? (int)i : -(1 << 24);   // a dead row fails every p >= 0 test
                 a_j[jn] = (int)j;
-                a_off[jn] = ((n * (uint32_t)a.P + i) * (uint32_t)a.Q + j) * (uint32_t)K + (uint32_t)a_k[jn];
+                a_off[jn] = (((n * (uint32_t)P + i) * (uint32_t)Q + j) * (uint32_t)K + (uint32_t)a_k[jn]) * 2u;
             }
+#pragma unroll
+            for (int jn = 0; jn < B_INSTR; ++jn)
+                w_vt[jn] = rq_c0 + b_c[jn] >= C ? 0x80000000u : w_lane[jn];
         }
-        const PhaseArg& ph = a.ph[rq_pi];
-        q_dr = ph.dr0 - ar;
-        q_dt = ph.dt0 - at;
-        q_tapoff = (uint32_t)(q_dr * a.Q + q_dt) * (uint32_t)K + (uint32_t)k0;
-        q_wtap = ((ph.r0 + ar * s) * a.S + (ph.t0 + at * s)) * C;
+        if (new_tap) {          // once per tap: padding checks and dy offsets
+            new_tap = false;
+            const int dr = rq_dr0 - ar;
+            const int dt = rq_dt0 - at;
+            const uint32_t tapoff = (uint32_t)((dr * Q + dt) * K) * 2u;
+#pragma unroll
+            for (int jn = 0; jn < A_INSTR; ++jn) {
+                const bool ok = ((unsigned)(a_i[jn] + dr) < (unsigned)P) & ((unsigned)(a_j[jn] + dt) < (unsigned)Q);
+                dy_vo[jn] = ok ? a_off[jn] + tapoff : 0x80000000u;
+            }
+#pragma unroll
+            for (int jn = 0; jn < B_INSTR; ++jn)
+                w_vo[jn] = w_vt[jn];
+            q_wtap = (uint32_t)(rq_wt0 + ar * s * SC + at * s * C + rq_c0) * 2u;
+        }
+        if (k0 + BK > K) {      // ragged last k step of a tap: mask the lanes past K
+#pragma unroll
+            for (int jn = 0; jn < A_INSTR; ++jn)
+                dy_vo[jn] = k0 + a_k[jn] >= K ? 0x80000000u : dy_vo[jn];
+#pragma unroll
+            for (int jn = 0; jn < B_INSTR; ++jn)
+                w_vo[jn] = k0 + b_k[jn] >= K ? 0x80000000u : w_vo[jn];
+        }
         q_base = lds_u32 + (uint32_t)(buf * STAGE);
-        rq_buf = buf;
         return true;
     };
     // Issue part `part` (of 4) of the prepared slice's direct-to-LDS loads:
@@ -359,17 +406,10 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                 continue;
             if (x < A_INSTR) {
                 const int jn = x;
-                const uint32_t bad = (uint32_t)(k0 + a_k[jn] >= K) |
-                                     (uint32_t)((unsigned)(a_i[jn] + q_dr) >= (unsigned)a.P) |
-                                     (uint32_t)((unsigned)(a_j[jn] + q_dt) >= (unsigned)a.Q);
-                dma16(dy_desc, out_of_range_if(bad, (a_off[jn] + q_tapoff) * 2u),
-                      q_base + (uint32_t)((jn * NW + wave) * 1024));
+                dma16(dy_desc, dy_vo[jn], (uint32_t)k0 * 2u, q_base + (uint32_t)((jn * NW + wave) * 1024));
             } else {
                 const int jn = x - A_INSTR;
-                const int k = k0 + b_k[jn];
-                const int c = rq_c0 + b_c[jn];
-                const uint32_t bad = (uint32_t)(k >= K) | (uint32_t)(c >= C);
-                dma16(w_desc, out_of_range_if(bad, (uint32_t)(k * RSC + q_wtap + c) * 2u),
+                dma16(w_desc, w_vo[jn], q_wtap + (uint32_t)(k0 * RSC) * 2u,
                       q_base + (uint32_t)(A_BYTES + (jn * NW + wave) * 1024));
             }
         }
@@ -379,27 +419,22 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     // Exactly zps stores per request, so the waits below can count them;
     // those outside the tile's share are dropped by the range check.
     auto issue_zero = [&]() {
-        ops += LD;              // this request's loads are all issued
-        last_load0 = rq_buf == 0 ? ops : last_load0;   // selects, not branches
-        last_load1 = rq_buf == 1 ? ops : last_load1;
-        last_load2 = rq_buf == 2 ? ops : last_load2;
-        ops += (uint32_t)a.zps;
-        const int si = rq_niter - rq_left;
-        for (int jz = 0; jz < a.zps; ++jz) {
-            const int idx = si * a.zps + jz;
-            const uint32_t stripe = (uint32_t)rq_tile * (uint32_t)a.zt + (uint32_t)idx;
-            zero_stripe(idx < a.zt && stripe < a.zabsorbed ? stripe : 0xffffffffu);
+        const uint32_t first = (uint32_t)(rq_niter - rq_left) * zps;
+        for (uint32_t jz = 0; jz < zps; ++jz) {
+            const uint32_t idx = first + jz;
+            const uint32_t stripe = (uint32_t)rq_tile * zt + idx;
+            zero_stripe(stripe, idx < zt && stripe < zabsorbed);
         }
     };
-    // Advance the cursor past the issued slice. Taps innermost: consecutive
-    // slices re-read the same dy rows (shifted by one tap), so the repeats hit in L2.
+    // Advance the cursor past the issued slice: k innermost, then taps.
     auto finish_request = [&]() {
-        const PhaseArg& ph = a.ph[rq_pi];
-        if (++at == ph.nt) {
-            at = 0;
-            if (++ar == ph.nr) {
-                ar = 0;
-                k0 += BK;
+        k0 += BK;
+        if (k0 >= K) {
+            k0 = 0;
+            new_tap = true;
+            if (++at == rq_nt) {
+                at = 0;
+                ++ar;
             }
         }
         --rq_left;
@@ -558,18 +593,19 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             }
         }
     };
-    // vector-memory operations of one epilogue
-    constexpr uint32_t kEpiStores = FM * EST;
-    constexpr uint32_t kEpiZLoads = FM * FN * 4;
 
     // ---- the walk. The k-th slice of the stream lives in LDS stage k % 3:
     // rbuf is the stage of the next request, cbuf that of the next slice to
     // compute; requests run two slices ahead.
-    int rbuf = 0, cbuf = 0;
-    if (request_next(rbuf))
+    int rbuf = 0, cbuf = 0, inflight = 0;   // inflight: slices requested, not yet computed
+    if (request_next(rbuf)) {
         rbuf = 1;
-    if (request_next(rbuf))
+        ++inflight;
+    }
+    if (request_next(rbuf)) {
         rbuf = 2;
+        ++inflight;
+    }
     const int epi = a.epi;
     for (int round = 0;; ++round) {
         const int tile = round * G + slot;
@@ -579,8 +615,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             const uint32_t first = a.zabsorbed + (uint32_t)(tile - a.gemm_tiles) * kZeroChunkStripes;
 #pragma unroll
             for (int u = 0; u < kZeroChunkStripes; ++u)
-                zero_stripe(first + u);
-            ops += kZeroChunkStripes;
+                zero_stripe(first + u, first + u < a.zstripes);
             continue;
         }
         const Tile t = decode(tile);
@@ -594,10 +629,18 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                 for (int e = 0; e < 16; ++e)
                     acc[fn][fm][e] = 0.0f;
         for (int it = 0; it < t.niter; ++it) {
-            // This slice must have landed; whatever was issued after its last
-            // load (later requests, zero stores, the previous tile's
-            // epilogue) may still be in flight.
-            wait_vmcnt_at_most(ops - (cbuf == 0 ? last_load0 : (cbuf == 1 ? last_load1 : last_load2)));
+            // This slice must have landed. Memory operations complete in issue
+            // order, and after its last load came its zps zero stores and, if
+            // issued, the next request (LD loads, zps stores); an epilogue in
+            // between only makes the wait stricter.
+            if (inflight >= 2) {
+                if (zps != 0)
+                    wait_vmcnt<LD + 2 * kMaxZeroPerSlice>();
+                else
+                    wait_vmcnt<LD>();
+            } else {
+                wait_vmcnt<0>();
+            }
             __syncthreads();     // every wave's part of the slice is in LDS, and every
                                  // wave is done with the stage the next request reuses
             const bool more = prepare_next(rbuf);
@@ -605,13 +648,14 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             if (more) {
                 finish_request();
                 rbuf = rbuf == 2 ? 0 : rbuf + 1;
+            } else {
+                --inflight;
             }
             cbuf = cbuf == 2 ? 0 : cbuf + 1;
         }
 
         // ---- epilogue (one specialisation per kind; the kind is uniform),
         // staged through the stage of the slice just computed
-        ops += kEpiStores + (epi != kEpiNone ? kEpiZLoads : 0u);
         const int sdone = cbuf == 0 ? 2 : cbuf - 1;
         switch (epi) {
         case kEpiDRelu: epilogue(EpiTag<kEpiDRelu>{}, t, ph, sdone); break;
@@ -643,7 +687,6 @@ int resident(void)
 
 // The compiled tile configurations: (BM, BN, WM, WN).
 #define CBW_TILE_CONFIGS(X) \
-    X(256, 128, 2, 2)       \
     X(128, 128, 2, 2)       \
     X(256, 64, 4, 1)        \
     X(128, 64, 2, 2)        \
