@@ -33,8 +33,10 @@
 //   dy slice: BM rows x 128 bytes; chunk c of row m at position c ^ ((m>>1)&7)
 //             (16 lanes reading one chunk of 16 consecutive rows hit 16
 //             distinct 16-byte bank groups of the 256-byte bank window)
-//   w  slice: 64 rows x 2*BN bytes; chunk c of row k at position c ^ 2*(k&3)
-//             (a 16-lane transpose group's four rows hit distinct banks)
+//   w  slice: 64 rows x 2*BN bytes; chunk c of row k at position
+//             c ^ 4*(k&3) (c ^ 4*((k>>1)&1) for 128-byte rows)
+//             (the 32 lanes of half a transpose read cover 256 distinct bytes
+//             of the bank window)
 //
 // Persistent walk: the grid holds as many workgroups as can be resident;
 // each walks its tiles in rounds, and the slice stream runs across tile
@@ -129,6 +131,17 @@ __device__ inline void wait_vmcnt()
 __device__ inline int dy_swizzle(int row)
 {
     return (row >> 1) & 7;
+}
+
+// Chunk permutation of filter row k in LDS (rows of 2*BN bytes). A
+// transpose read covers, per 32-lane half, four consecutive rows x four
+// consecutive chunks; the permutation sends these 16 (row, chunk) pairs to
+// 16 distinct 16-byte bank groups of the 256-byte bank window.
+template <int B_ROW>
+__device__ inline int w_swizzle(int k)
+{
+    static_assert(B_ROW == 128 || B_ROW % 256 == 0, "filter rows of 128 bytes or whole bank windows");
+    return B_ROW == 128 ? 4 * ((k >> 1) & 1) : 4 * (k & 3);
 }
 
 constexpr int kEpiNone = 0;
@@ -309,7 +322,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     // DMA block b = jn*NW + wave of a dy slice covers tile rows 8b..8b+7; lane l
     // fills row 8b + l/8 at chunk position l%8, holding logical chunk
     // (l%8) ^ dy_swizzle(row). Byte 16*l of block jn*NW + wave of a filter
-    // slice is row k, position p, holding logical chunk p ^ 2*(k & 3).
+    // slice is row k, position p, holding logical chunk p ^ w_swizzle(k).
     int a_k[A_INSTR], b_k[B_INSTR], b_c[B_INSTR];
     uint32_t w_lane[B_INSTR];  // byte offset of the lane's filter element within a slice
 #pragma unroll
@@ -321,7 +334,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         const int k = byte / B_ROW;
         const int pos = (byte % B_ROW) / 16;
         b_k[jn] = k;
-        b_c[jn] = (pos ^ (2 * (k & 3))) * 8;
+        b_c[jn] = (pos ^ w_swizzle<B_ROW>(k)) * 8;
         w_lane[jn] = (uint32_t)(k * RSC + b_c[jn]) * 2u;
     }
     uint32_t a_off[A_INSTR];   // byte offset of dy[n, i, j, chunk*8], modulo 2^32: a
@@ -463,7 +476,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     for (int fn = 0; fn < FN; ++fn) {
         const int cl = wn * TN + fn * 32 + (g & 1) * 16 + 4 * qq;   // first channel this lane reads
         const int krow = (g >> 1) * 8 + rr;
-        a_frag[fn] = A_BYTES + krow * B_ROW + (((cl >> 3) ^ (2 * rr)) * 16) + (cl & 7) * 2;
+        a_frag[fn] = A_BYTES + krow * B_ROW + (((cl >> 3) ^ w_swizzle<B_ROW>(krow)) * 16) + (cl & 7) * 2;
     }
 
     float16_t acc[FN][FM];
@@ -533,6 +546,8 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     constexpr int EST = 32 / PPI;         // store instructions per pixel group
     static_assert(NW * EBLK <= STAGE, "the staging blocks fit in one stage");
     static_assert(CH >= 2 && CH <= 64 && 64 % CH == 0, "whole pixel rows per store");
+    constexpr int kEpiStores = FM * EST;     // stores of one epilogue (per wave)
+    static_assert(LD + 2 * kMaxZeroPerSlice + kEpiStores < 64, "vmcnt range");
     const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(a.epi != kEpiNone ? a.z : a.dx, a.dx_bytes);
     auto epilogue = [&](auto tag, const Tile& t, const PhaseArg& ph, int stage) {
         constexpr int E = decltype(tag)::value;
@@ -598,6 +613,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     // rbuf is the stage of the next request, cbuf that of the next slice to
     // compute; requests run two slices ahead.
     int rbuf = 0, cbuf = 0, inflight = 0;   // inflight: slices requested, not yet computed
+    int post_epi = 0;                        // slices left whose loads precede the last epilogue
     if (request_next(rbuf)) {
         rbuf = 1;
         ++inflight;
@@ -630,17 +646,26 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                     acc[fn][fm][e] = 0.0f;
         for (int it = 0; it < t.niter; ++it) {
             // This slice must have landed. Memory operations complete in issue
-            // order, and after its last load came its zps zero stores and, if
-            // issued, the next request (LD loads, zps stores); an epilogue in
-            // between only makes the wait stricter.
+            // order, and after its last load came its zps zero stores, the
+            // next request (LD loads, zps stores) when it was issued, and, in
+            // the first two slices after an epilogue, that epilogue's kEpiStores
+            // stores (its z loads only make the wait stricter).
             if (inflight >= 2) {
-                if (zps != 0)
-                    wait_vmcnt<LD + 2 * kMaxZeroPerSlice>();
-                else
-                    wait_vmcnt<LD>();
+                if (zps != 0) {
+                    if (post_epi > 0)
+                        wait_vmcnt<LD + 2 * kMaxZeroPerSlice + kEpiStores>();
+                    else
+                        wait_vmcnt<LD + 2 * kMaxZeroPerSlice>();
+                } else {
+                    if (post_epi > 0)
+                        wait_vmcnt<LD + kEpiStores>();
+                    else
+                        wait_vmcnt<LD>();
+                }
             } else {
                 wait_vmcnt<0>();
             }
+            post_epi = post_epi > 0 ? post_epi - 1 : 0;
             __syncthreads();     // every wave's part of the slice is in LDS, and every
                                  // wave is done with the stage the next request reuses
             const bool more = prepare_next(rbuf);
@@ -655,7 +680,9 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         }
 
         // ---- epilogue (one specialisation per kind; the kind is uniform),
-        // staged through the stage of the slice just computed
+        // staged through the stage of the slice just computed. The two slices
+        // in flight were requested before it.
+        post_epi = 2;
         const int sdone = cbuf == 0 ? 2 : cbuf - 1;
         switch (epi) {
         case kEpiDRelu: epilogue(EpiTag<kEpiDRelu>{}, t, ph, sdone); break;
