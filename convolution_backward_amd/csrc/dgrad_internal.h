@@ -75,6 +75,13 @@ struct KernelArgs {
     int zt;              // zero stripes per GEMM tile (<= zps * fewest slices of a tile)
     FastDiv div_c8;      // division by C/8
     ZeroPhaseArg zph[kMaxPhasesPerLaunch];
+    // Companion zero phases: when the launch's only GEMM phase and its zero
+    // phases share one lattice shape, zero pixel (n, ph' + s*i, pw' + s*j) lies
+    // a fixed comp_delta[q] elements from GEMM pixel (n, ph + s*i, pw + s*j);
+    // the epilogue stores those zeros beside each GEMM chunk (and the zero
+    // list above is empty).
+    int ncomp;
+    int comp_delta[kMaxPhasesPerLaunch];
 };
 
 // Zero stripes a slice request may carry (each is one 16-byte store per thread).

@@ -230,6 +230,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     const uint32_t zps = pin((uint32_t)a.zps);
     const uint32_t zt = pin((uint32_t)a.zt);
     const uint32_t zabsorbed = pin(a.zabsorbed);
+    const int ncomp = pin(a.ncomp);
 
     const __amdgpu_buffer_rsrc_t dx_rsrc = make_rsrc(a.dx, a.dx_bytes);
     const i32x4 dy_desc = raw_descriptor(a.dy, a.dy_bytes);
@@ -604,7 +605,11 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                 const int m = t.m0 + wm * TM + fm * 32 + pr;
                 const int c = cw + q * 8;
                 const uint32_t bad = (uint32_t)(m >= ph.M) | (uint32_t)(c >= C);
-                __builtin_amdgcn_raw_buffer_store_b128(v, dx_rsrc, out_of_range_if(bad, (pixel_offset(ph, m) + (uint32_t)c) * 2u), 0, 0);
+                const uint32_t off = (pixel_offset(ph, m) + (uint32_t)c) * 2u;
+                __builtin_amdgcn_raw_buffer_store_b128(v, dx_rsrc, out_of_range_if(bad, off), 0, 0);
+                const u32x4 zero{0u, 0u, 0u, 0u};
+                for (int qc = 0; qc < ncomp; ++qc)   // companion zero pixels (same lattice point)
+                    __builtin_amdgcn_raw_buffer_store_b128(zero, dx_rsrc, out_of_range_if(bad, off + (uint32_t)a.comp_delta[qc] * 2u), 0, 0);
             }
         }
     };
