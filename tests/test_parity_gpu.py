@@ -227,3 +227,41 @@ def test_autotune_off_uses_heuristic():
         assert cached and got == want
     finally:
         cb.conv2d_dgrad_set_autotune(prev)
+
+
+# ---------------------------------------------------------------- maximum sizes
+
+def _int8_inputs(cfg, seed):
+    """Small-integer dy and w drawn as int8 (host memory stays near the tensor
+    size): every product and partial sum is an exact fp16/fp32 integer."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dy = rng.integers(-2, 3, size=(cfg.N, cfg.P, cfg.Q, cfg.K), dtype=np.int8).astype(np.float16)
+    w = rng.integers(-2, 3, size=(cfg.K, cfg.R, cfg.S, cfg.C), dtype=np.int8).astype(np.float16)
+    return {"dy": dy, "w": w, "z": None}
+
+
+# One tensor just below the 2^30-element limit in each case, so byte offsets,
+# the last pixels and (for 1x1 stride 2) the companion zero stores reach the
+# top of the 32-bit offset range.
+MAX_SHAPES = [
+    ("dx_1x1_s1", (63, 128, 128, 1024, 64, 1, 1, 1, 0)),       # dx 1,056,964,608 elements
+    ("dy_1x1_s1", (63, 128, 128, 64, 1024, 1, 1, 1, 0)),       # dy 1,056,964,608 elements
+    ("dx_3x3_s2", (40, 448, 448, 128, 64, 3, 3, 2, 1)),        # dx 1,027,604,480 elements, 4 phases
+    ("dx_1x1_s2", (20, 448, 448, 256, 64, 1, 1, 2, 0)),        # dx 1,027,604,480 elements, 3 zero phases
+]
+
+
+@pytest.mark.parametrize("name,shape", MAX_SHAPES, ids=[n for n, _ in MAX_SHAPES])
+def test_maximum_sizes_bit_exact(name, shape):
+    cfg = small_config(*shape, name=name)
+    assert max(cfg.N * cfg.P * cfg.Q * cfg.K, cfg.N * cfg.H * cfg.W * cfg.C) < 2 ** 30
+    inp = _int8_inputs(cfg, seed=17)
+    note(f"maximum size {name} {shape}")
+    gpu = run(cfg, inp)
+    rows = sample_rows(cfg, 1500, seed=5)
+    last = cfg.N * cfg.H * cfg.W
+    rows = np.unique(np.concatenate([rows, np.arange(last - 64, last)]))
+    ref16 = oracle.round_to_half(ref_rows(cfg, inp, rows))
+    _bits_equal(gpu.reshape(-1, cfg.C)[rows], ref16)
+    if cfg.stride == 2 and cfg.R == 1:    # the three zero lattices, everywhere
+        assert not np.any(gpu[:, 1::2, :, :]) and not np.any(gpu[:, :, 1::2, :])
