@@ -49,6 +49,9 @@ def _bind(lib):
     lib.conv2d_dgrad_config_name.argtypes = [i, ctypes.c_char_p, i]
     lib.conv2d_dgrad_query_config.argtypes = [i] * 10 + [ip, ip]
     lib.conv2d_dgrad_set_autotune.argtypes = [i]
+    lib.conv2d_dgrad_set_streamk.argtypes = [i]
+    lib.conv2d_dgrad_streamk_launches.argtypes = []
+    lib.conv2d_dgrad_streamk_launches.restype = ctypes.c_longlong
     lib.conv2d_dgrad_cache_clear.argtypes = []
     lib.conv2d_dgrad_cache_size.argtypes = []
     lib.conv2d_dgrad_cache_save.argtypes = [ctypes.c_char_p]
@@ -61,7 +64,7 @@ def _bind(lib):
     lib.conv2d_dgrad_build_info.restype = ctypes.c_char_p
     for name in ("conv2d_dgrad_nhwc", "conv2d_dgrad_nhwc_config", "conv2d_dgrad_num_configs",
                  "conv2d_dgrad_config_name", "conv2d_dgrad_query_config", "conv2d_dgrad_set_autotune",
-                 "conv2d_dgrad_cache_clear", "conv2d_dgrad_cache_size", "conv2d_dgrad_cache_save",
+                 "conv2d_dgrad_set_streamk", "conv2d_dgrad_streamk_launches", "conv2d_dgrad_cache_clear", "conv2d_dgrad_cache_size", "conv2d_dgrad_cache_save",
                  "conv2d_dgrad_cache_load", "conv2d_dgrad_plan", "conv2d_dgrad_check"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -153,6 +156,20 @@ def conv2d_dgrad_set_autotune(on: bool) -> bool:
     return bool(get_lib().conv2d_dgrad_set_autotune(1 if on else 0))
 
 
+def conv2d_dgrad_set_streamk(mode: int) -> int:
+    """0 never split the reduction, 1 whenever eligible, 2 (default) when it pays;
+    returns the previous mode."""
+    prev = get_lib().conv2d_dgrad_set_streamk(int(mode))
+    if prev < 0:
+        raise DgradError(INVALID_ARGUMENT, conv2d_dgrad_last_error())
+    return prev
+
+
+def conv2d_dgrad_streamk_launches() -> int:
+    """Kernel launches enqueued with a stream-K split since the library loaded."""
+    return int(get_lib().conv2d_dgrad_streamk_launches())
+
+
 def conv2d_dgrad_cache_clear():
     return _check(get_lib().conv2d_dgrad_cache_clear())
 
@@ -214,6 +231,7 @@ def dgrad(dy, w, H, W, stride, pad, epilogue=EPI_NONE, z=None, config_id=None, o
 __all__ = [
     "conv2d_dgrad_nhwc", "conv2d_dgrad_nhwc_config", "conv2d_dgrad_check", "conv2d_dgrad_num_configs",
     "conv2d_dgrad_config_name", "conv2d_dgrad_query_config", "conv2d_dgrad_set_autotune",
+    "conv2d_dgrad_set_streamk", "conv2d_dgrad_streamk_launches",
     "conv2d_dgrad_cache_clear", "conv2d_dgrad_cache_size", "conv2d_dgrad_cache_save", "conv2d_dgrad_cache_load",
     "conv2d_dgrad_plan", "conv2d_dgrad_last_error", "conv2d_dgrad_build_info", "dgrad", "get_lib",
     "DgradError", "EPI_NONE", "EPI_DRELU", "EPI_DHARDSWISH",

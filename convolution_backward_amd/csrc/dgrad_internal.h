@@ -82,6 +82,18 @@ struct KernelArgs {
     // list above is empty).
     int ncomp;
     int comp_delta[kMaxPhasesPerLaunch];
+    // Stream-K: the launch's GEMM slices (tile after tile, phase i's first
+    // at slice_begin[i]) are cut into `grid` equal contiguous ranges, one per
+    // workgroup, so a tile may be shared by consecutive workgroups. Each
+    // share of a split tile leaves its fp32 partial sums in workspace slot
+    // [tile][segment]; the last share to arrive (per-tile counter) adds the
+    // shares in segment order, runs the epilogue and resets the counter.
+    int sk;              // 1: stream-K split (launches without zero phases only)
+    int sk_slices;       // GEMM slices of the launch
+    int sk_maxseg;       // workspace slots per tile
+    float* sk_part;      // [gemm_tiles][sk_maxseg][BM*BN] fp32, in register order
+    int* sk_count;       // [gemm_tiles] arrival counters, zero between launches
+    int slice_begin[kMaxPhasesPerLaunch];   // first slice of each GEMM phase's tiles
 };
 
 // Zero stripes a slice request may carry (each is one 16-byte store per thread).
@@ -96,6 +108,7 @@ struct TileConfig {
     int WM, WN;          // wave grid (64-lane waves) over the tile
     const char* name;
     int lds_bytes;
+    bool streamk;        // compiled with a stream-K variant
 };
 
 int num_tile_configs();

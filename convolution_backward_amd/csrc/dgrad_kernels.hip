@@ -194,7 +194,7 @@ struct EpiTag {
     static constexpr int value = E;
 };
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool SK>
 __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
 {
     constexpr int BK = 64;
@@ -232,10 +232,10 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     const int ksteps = (K + BK - 1) / BK;
     const int SC = pin(a.S * C);          // filter elements per tap row
     const int RSC = pin(a.R * SC);        // filter elements per k
-    const uint32_t zps = pin((uint32_t)a.zps);
-    const uint32_t zt = pin((uint32_t)a.zt);
-    const uint32_t zabsorbed = pin(a.zabsorbed);
-    const int ncomp = pin(a.ncomp);
+    const uint32_t zps = SK ? 0u : pin((uint32_t)a.zps);
+    const uint32_t zt = SK ? 0u : pin((uint32_t)a.zt);
+    const uint32_t zabsorbed = SK ? 0u : pin(a.zabsorbed);
+    const int ncomp = SK ? 0 : pin(a.ncomp);
 
     const __amdgpu_buffer_rsrc_t dx_rsrc = make_rsrc(a.dx, a.dx_bytes);
     const i32x4 dy_desc = raw_descriptor(a.dy, a.dy_bytes);
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     const int G = gridDim.x;
     const int slot = xcd_remap(blockIdx.x, G, a.group, a.xcd_mode);
     struct Tile {
-        int pi, m0, c0, niter;
+        int pi, m0, c0, niter, s0;   // s0: the tile's first slice in the launch's numbering
     };
     // GEMM tile `tile` (< gemm_tiles): its phase, first lattice row, first channel, slices.
     auto decode = [&](int tile) -> Tile {
@@ -263,7 +263,45 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             tn = local / a.ph[pi].tiles_m;
             tm = local - tn * a.ph[pi].tiles_m;
         }
-        return Tile{pi, tm * BM, tn * BN, a.ph[pi].nr * a.ph[pi].nt * ksteps};
+        const int niter = a.ph[pi].nr * a.ph[pi].nt * ksteps;
+        return Tile{pi, tm * BM, tn * BN, niter, a.slice_begin[pi] + local * niter};
+    };
+
+    // ---- work segments: slices [lo, hi) of one tile. Without stream-K the
+    // k-th segment of this workgroup is the whole tile k*G + slot. With it
+    // (segment() below), workgroup `slot` owns slices
+    // [floor(slot*T/G), floor((slot+1)*T/G)) of the launch's T slices, tile
+    // after tile.
+    struct Seg {
+        int tile, lo, hi;
+        bool ok;
+    };
+    const uint32_t skT = (uint32_t)a.sk_slices;
+    auto sk_start = [&](uint32_t w) -> uint32_t { return (uint32_t)(((uint64_t)w * skT) / (uint32_t)G); };
+    auto sk_owner = [&](uint32_t sl) -> uint32_t {   // the workgroup whose range holds slice sl
+        return (uint32_t)((((uint64_t)sl + 1) * (uint32_t)G - 1) / skT);
+    };
+    auto segment = [&](int k, Tile& t) -> Seg {
+        // this workgroup's range and its first tile (recomputed at each
+        // segment boundary rather than held in registers through the loop)
+        const uint32_t sk_s0 = sk_start((uint32_t)slot);
+        const uint32_t sk_s1 = sk_start((uint32_t)slot + 1);
+        if (sk_s1 <= sk_s0)
+            return Seg{0, 0, 0, false};
+        int pi = 0;
+        for (int i = 1; i < a.nphases; ++i)
+            if (sk_s0 >= (uint32_t)a.slice_begin[i])
+                pi = i;
+        const int niter0 = a.ph[pi].nr * a.ph[pi].nt * ksteps;
+        const int tile = a.ph[pi].tile_begin + (int)((sk_s0 - (uint32_t)a.slice_begin[pi]) / (uint32_t)niter0) + k;
+        if (tile >= a.gemm_tiles)
+            return Seg{0, 0, 0, false};
+        t = decode(tile);
+        const int lo = k == 0 ? (int)(sk_s0 - (uint32_t)t.s0) : 0;
+        if ((uint32_t)(t.s0 + lo) >= sk_s1)
+            return Seg{0, 0, 0, false};
+        const int hi = (uint32_t)(t.s0 + t.niter) <= sk_s1 ? t.niter : (int)(sk_s1 - (uint32_t)t.s0);
+        return Seg{tile, lo, hi, true};
     };
 
     // dx element offset of lattice row m of phase ph (pixel n, h = ph + s*i, w = pw + s*j)
@@ -358,19 +396,33 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     uint32_t q_base = 0;       // LDS address of the stage being filled
     // Pick the next slice of the stream; false when the stream is exhausted.
     auto prepare_next = [&](int buf) -> bool {
-        while (rq_left == 0) {  // move to the next tile
-            const int tile = rq_round * G + slot;
-            if (tile >= a.gemm_tiles)
-                return false;
+        while (rq_left == 0) {  // move to the next segment
+            Tile t;
+            Seg g;
+            if constexpr (SK) {
+                g = segment(rq_round, t);
+                if (!g.ok)
+                    return false;
+            } else {
+                const int tile = rq_round * G + slot;
+                if (tile >= a.gemm_tiles)
+                    return false;
+                t = decode(tile);
+                g = Seg{tile, 0, t.niter, true};
+            }
             ++rq_round;
-            const Tile t = decode(tile);
             rq_c0 = t.c0;
-            rq_left = t.niter;
-            rq_niter = t.niter;
-            rq_tile = tile;
-            ar = at = k0 = 0;
-            new_tap = true;
+            rq_left = g.hi - g.lo;
+            rq_niter = g.hi - g.lo;
+            rq_tile = g.tile;
             const PhaseArg& ph = a.ph[t.pi];
+            {   // the cursor at slice g.lo of the tile (k innermost, then taps)
+                const int tap = g.lo / ksteps;
+                ar = tap / ph.nt;
+                at = tap - ar * ph.nt;
+                k0 = (g.lo - tap * ksteps) * BK;
+            }
+            new_tap = true;
             rq_dr0 = pin(ph.dr0);
             rq_dt0 = pin(ph.dt0);
             rq_nt = pin(ph.nt);
@@ -619,6 +671,97 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         }
     };
 
+    // ---- stream-K fix-up for a share of a split tile. The share's fp32
+    // partial sums go to workspace slot [tile][segment] in register order
+    // (16-byte group q of thread tid at float offset (q*NT + tid)*4), and the
+    // tile's counter counts the arrival. The last share to arrive (no share
+    // ever waits for another) adds all shares in segment order, its own from
+    // registers, leaves the sum in acc, resets the counter and returns true.
+    // A share that finds every other share already arrived is the last one
+    // without writing its own partial sums (nor arriving).
+    // The workspace lives in uncached device memory and every access to it is
+    // system-scope (sc0 sc1), so neither side needs an L2 writeback or
+    // invalidate: a share's stores have reached memory once its vmcnt drains,
+    // which precedes its arrival on the counter.
+    auto sk_fixup = [&](int tile, const Tile& t, int stage) -> bool {
+        constexpr int NQ = FN * FM * 4;   // 16-byte groups of accumulators per thread
+        constexpr int QB = NQ < 8 ? NQ : 8;   // groups summed per pass (loads in flight per thread)
+        constexpr int kSys = 17;          // cache policy sc0 sc1
+        static_assert(NQ % QB == 0, "accumulator groups per pass");
+        const uint32_t first = sk_owner((uint32_t)t.s0);
+        const int seg = (int)((uint32_t)slot - first);
+        const int nseg = (int)(sk_owner((uint32_t)(t.s0 + t.niter - 1)) - first) + 1;
+        constexpr uint32_t kSegBytes = (uint32_t)BM * BN * 4;
+        const __amdgpu_buffer_rsrc_t ws =
+            make_rsrc(a.sk_part + (size_t)tile * (size_t)a.sk_maxseg * (size_t)(BM * BN), (uint32_t)a.sk_maxseg * kSegBytes);
+        const uint32_t lane_off = (uint32_t)tid * 16u;
+        __attribute__((address_space(3))) int* flag = (__attribute__((address_space(3))) int*)((lds_char*)lds + stage * STAGE);
+        __syncthreads();                  // no wave reads the stage's operands any more
+        if (tid == 0)
+            *flag = __hip_atomic_load(&a.sk_count[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nseg - 1 ? 1 : 0;
+        __syncthreads();
+        // one value for the whole workgroup: taken from the first lane so the
+        // branches below are uniform in the compiler's eyes too
+        if (__builtin_amdgcn_readfirstlane(*flag) == 0) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int g = (fn * FM + fm) * 4 + q;
+                        const float4_t v{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2], acc[fn][fm][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws,
+                                                               (uint32_t)seg * kSegBytes + (uint32_t)(g * NT) * 16u + lane_off, 0, kSys);
+                    }
+            wait_vmcnt<0>();              // this wave's partial sums are in memory
+            __syncthreads();              // ... and every wave's; every wave has read the flag
+            if (tid == 0) {
+                const int old = __hip_atomic_fetch_add(&a.sk_count[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *flag = old == nseg - 1 ? 1 : 0;
+            }
+            __syncthreads();
+            if (__builtin_amdgcn_readfirstlane(*flag) == 0)
+                return false;
+        }
+#pragma unroll
+        for (int g0 = 0; g0 < NQ; g0 += QB) {
+            float4_t sum[QB];
+#pragma unroll
+            for (int u = 0; u < QB; ++u)
+                sum[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int sg = 0; sg < nseg; ++sg) {
+                float4_t v[QB];
+                if (sg == seg) {
+#pragma unroll
+                    for (int u = 0; u < QB; ++u) {
+                        const int g = g0 + u, fn = g / (FM * 4), fm = (g / 4) % FM, q = g % 4;
+                        v[u] = float4_t{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2], acc[fn][fm][4 * q + 3]};
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < QB; ++u)
+                        v[u] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                ws, (uint32_t)sg * kSegBytes + (uint32_t)((g0 + u) * NT) * 16u + lane_off, 0, kSys));
+                }
+#pragma unroll
+                for (int u = 0; u < QB; ++u)
+                    sum[u] += v[u];
+            }
+#pragma unroll
+            for (int u = 0; u < QB; ++u) {
+                const int g = g0 + u, fn = g / (FM * 4), fm = (g / 4) % FM, q = g % 4;
+                acc[fn][fm][4 * q] = sum[u][0];
+                acc[fn][fm][4 * q + 1] = sum[u][1];
+                acc[fn][fm][4 * q + 2] = sum[u][2];
+                acc[fn][fm][4 * q + 3] = sum[u][3];
+            }
+        }
+        if (tid == 0)
+            __hip_atomic_store(&a.sk_count[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    };
+
     // ---- the walk. The k-th slice of the stream lives in LDS stage k % 3:
     // rbuf is the stage of the next request, cbuf that of the next slice to
     // compute; requests run two slices ahead.
@@ -634,17 +777,26 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     }
     const int epi = a.epi;
     for (int round = 0;; ++round) {
-        const int tile = round * G + slot;
-        if (tile >= a.total_tiles)
-            break;
-        if (tile >= a.gemm_tiles) {   // a chunk of zero stripes (no request is in flight any more)
-            const uint32_t first = a.zabsorbed + (uint32_t)(tile - a.gemm_tiles) * kZeroChunkStripes;
+        Tile t;
+        Seg g;
+        if constexpr (SK) {
+            g = segment(round, t);
+            if (!g.ok)
+                break;
+        } else {
+            const int tile = round * G + slot;
+            if (tile >= a.total_tiles)
+                break;
+            if (tile >= a.gemm_tiles) {   // a chunk of zero stripes (no request is in flight any more)
+                const uint32_t first = a.zabsorbed + (uint32_t)(tile - a.gemm_tiles) * kZeroChunkStripes;
 #pragma unroll
-            for (int u = 0; u < kZeroChunkStripes; ++u)
-                zero_stripe(first + u, first + u < a.zstripes);
-            continue;
+                for (int u = 0; u < kZeroChunkStripes; ++u)
+                    zero_stripe(first + u, first + u < a.zstripes);
+                continue;
+            }
+            t = decode(tile);
+            g = Seg{tile, 0, t.niter, true};
         }
-        const Tile t = decode(tile);
         const PhaseArg& ph = a.ph[t.pi];
 
 #pragma unroll
@@ -654,7 +806,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
                     acc[fn][fm][e] = 0.0f;
-        for (int it = 0; it < t.niter; ++it) {
+        for (int it = g.lo; it < g.hi; ++it) {
             // This slice must have landed. Memory operations complete in issue
             // order, and after its last load came its zps zero stores, the
             // next request (LD loads, zps stores) when it was issued, and, in
@@ -691,9 +843,14 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
 
         // ---- epilogue (one specialisation per kind; the kind is uniform),
         // staged through the stage of the slice just computed. The two slices
-        // in flight were requested before it.
-        post_epi = 2;
+        // in flight were requested before it. A share of a split tile first
+        // leaves its partial sums; only the share that completes the tile goes on.
         const int sdone = cbuf == 0 ? 2 : cbuf - 1;
+        post_epi = 2;
+        if constexpr (SK) {
+            if ((g.lo != 0 || g.hi != t.niter) && !sk_fixup(g.tile, t, sdone))
+                continue;
+        }
         switch (epi) {
         case kEpiDRelu: epilogue(EpiTag<kEpiDRelu>{}, t, ph, sdone); break;
         case kEpiDHardswish: epilogue(EpiTag<kEpiDHardswish>{}, t, ph, sdone); break;
@@ -702,10 +859,24 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     }
 }
 
+// A stream-K variant exists for every configuration but 256x64/4x1, whose
+// uniform state does not fit the scalar register file once the fix-up is added.
+template <int BM, int BN, int WM, int WN>
+constexpr bool kHasStreamK = !(BM == 256 && BN == 64 && WM == 4);
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch(const KernelArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN>), dim3(a.grid), dim3(64 * WM * WN), 0, stream, a);
+    if constexpr (kHasStreamK<BM, BN, WM, WN>) {
+        if (a.sk) {
+            hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, true>), dim3(a.grid), dim3(64 * WM * WN), 0, stream, a);
+            return hipGetLastError();
+        }
+    } else {
+        if (a.sk)
+            return hipErrorInvalidValue;   // the host never plans this
+    }
+    hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, false>), dim3(a.grid), dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -714,11 +885,22 @@ template <int BM, int BN, int WM, int WN>
 int resident(void)
 {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN>),
+    // the stream-K instantiation must fit as many workgroups per CU (its
+    // ranges assume that many are resident); the smaller count of the two
+    int m = 1 << 20;
+    if constexpr (kHasStreamK<BM, BN, WM, WN>) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, true>),
+                                                         64 * WM * WN, 0) != hipSuccess) {
+            (void)hipGetLastError();
+            return 1;
+        }
+    }
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, false>),
                                                      64 * WM * WN, 0) != hipSuccess) {
         (void)hipGetLastError();
         return 1;
     }
+    n = n < m ? n : m;
     return n > 0 ? n : 1;
 }
 
@@ -731,7 +913,8 @@ int resident(void)
     X(256, 128, 4, 2)       \
     X(128, 256, 2, 4)
 
-#define CBW_CONFIG_ENTRY(BM, BN, WM, WN) {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN, 3 * (BM + BN) * 64 * 2},
+#define CBW_CONFIG_ENTRY(BM, BN, WM, WN) \
+    {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN, 3 * (BM + BN) * 64 * 2, kHasStreamK<BM, BN, WM, WN>},
 const TileConfig kConfigs[] = {CBW_TILE_CONFIGS(CBW_CONFIG_ENTRY)};
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs <= 64, "the launcher keeps per-config state for at most 64 configs");
@@ -742,11 +925,19 @@ template <int BM, int BN, int WM, int WN>
 int private_bytes(void)
 {
     hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN>)) != hipSuccess) {
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, false>)) != hipSuccess) {
         (void)hipGetLastError();
         return -1;
     }
-    return (int)attr.localSizeBytes;
+    size_t bytes = attr.localSizeBytes;
+    if constexpr (kHasStreamK<BM, BN, WM, WN>) {
+        if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, true>)) != hipSuccess) {
+            (void)hipGetLastError();
+            return -1;
+        }
+        bytes += attr.localSizeBytes;
+    }
+    return (int)bytes;
 }
 
 using LaunchFn = hipError_t (*)(const KernelArgs&, hipStream_t);

@@ -34,7 +34,8 @@
  * Ownership and execution. All tensor pointers are device pointers owned by
  * the caller, who keeps them alive until the enqueued work completes. Calls
  * are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
- * The library allocates no device memory and needs no workspace. dx is never
+ * The library allocates no device memory except the stream-K workspace (see
+ * conv2d_dgrad_set_streamk); the caller provides none. dx is never
  * read (it may hold anything, NaN included, before the call). dx must not
  * overlap dy, w or z.
  *
@@ -118,6 +119,41 @@ int conv2d_dgrad_query_config(int N, int H, int W, int C, int K, int R, int S,
 /* Autotuning on (1, the default unless the environment sets
  * CONV2D_DGRAD_AUTOTUNE=0) or off (0). Returns the previous setting. */
 int conv2d_dgrad_set_autotune(int on);
+
+/*
+ * Stream-K split of the reduction. A launch's reduction slices (all its GEMM
+ * tiles' slices, tile after tile) can be cut into equal contiguous ranges,
+ * one per workgroup, which helps when the tiles alone would leave workgroups
+ * idle. A tile shared by several workgroups is finished by the last of them
+ * to arrive, which adds the others' fp32 partial sums in a fixed order
+ * (results do not depend on timing, but differ in rounding from the unsplit
+ * sum). This is the "parallel split-k" that the "[CUTLASS] Conv2d dgrad" page
+ * (apache/tvm PR #10110) names as follow-up work.
+ *
+ * The partial sums need a workspace in uncached device memory: the library
+ * allocates one per device and stream on first use (outside graph capture)
+ * and never frees it; a larger one replaces it when needed, and the old one
+ * is kept for graphs that captured it. Under capture without a large enough
+ * workspace, or when allocation fails, the launch runs whole tiles. Calls on
+ * one stream are ordered by the stream; calls on different streams use
+ * different workspaces.
+ *
+ *   mode 0: never split.
+ *   mode 1: split every eligible launch (no zero phases, at least one GEMM
+ *           tile, partial sums within 1 GiB) as finely as the device allows.
+ *   mode 2 (default): the profiler times each tile configuration with and
+ *           without the split, and the table keeps the faster (table files
+ *           mark a split choice with "+sk" after the config name). For an
+ *           explicit config, or without profiling, a cost model splits when
+ *           that shortens the longest workgroup's work by 10% or more.
+ * Returns the previous mode, or -1 (with INVALID_ARGUMENT as the last error)
+ * for a mode outside 0..2. Choices already in the table are kept.
+ */
+int conv2d_dgrad_set_streamk(int mode);
+
+/* Kernel launches enqueued with a stream-K split since the library loaded
+ * (a diagnostic: it tells a caller whether the split was taken). */
+long long conv2d_dgrad_streamk_launches(void);
 
 /* Drop every cached choice; number of entries in the table. */
 int conv2d_dgrad_cache_clear(void);

@@ -170,6 +170,43 @@ def test_cache_save_load_roundtrip(tmp_path):
     assert cb.conv2d_dgrad_cache_size() == 0
 
 
+def test_cache_keeps_stream_k_choice(tmp_path):
+    """A table line may mark its choice as split ("+sk"); configurations
+    without a stream-K variant cannot carry the mark (the line is skipped)."""
+    cb.conv2d_dgrad_cache_clear()
+    names = [cb.conv2d_dgrad_config_name(i) for i in range(cb.conv2d_dgrad_num_configs())]
+    split_ok = names.index("256x128x64/4x2")
+    no_variant = names.index("256x64x64/4x1")
+    f = tmp_path / "table.txt"
+    f.write_text(f"256 7 7 512 512 3 3 1 1 2 none 256 {names[split_ok]}+sk\n"
+                 f"2 8 8 16 8 3 3 2 1 0 none 256 {names[no_variant]}+sk\n"
+                 f"2 8 8 16 8 3 3 1 1 0 none 256 {names[no_variant]}\n")
+    cb.conv2d_dgrad_cache_load(str(f))
+    assert cb.conv2d_dgrad_cache_size() == 2
+    cid, cached = cb.conv2d_dgrad_query_config(256, 7, 7, 512, 512, 3, 3, 1, 1, cb.EPI_DHARDSWISH)
+    assert cached and cid == split_ok
+    out = tmp_path / "saved.txt"
+    cb.conv2d_dgrad_cache_save(str(out))
+    lines = sorted(out.read_text().splitlines())
+    assert lines == sorted([f"256 7 7 512 512 3 3 1 1 2 none 256 {names[split_ok]}+sk",
+                            f"2 8 8 16 8 3 3 1 1 0 none 256 {names[no_variant]}"])
+    cb.conv2d_dgrad_cache_clear()
+
+
+def test_streamk_mode_setting():
+    prev = cb.conv2d_dgrad_set_streamk(0)
+    try:
+        assert cb.conv2d_dgrad_set_streamk(1) == 0
+        assert cb.conv2d_dgrad_set_streamk(2) == 1
+        with pytest.raises(cb.DgradError) as e:
+            cb.conv2d_dgrad_set_streamk(3)
+        assert e.value.code == cb.INVALID_ARGUMENT
+        assert cb.conv2d_dgrad_set_streamk(2) == 2
+    finally:
+        cb.conv2d_dgrad_set_streamk(prev)
+    assert cb.conv2d_dgrad_streamk_launches() == 0   # nothing launched without a GPU
+
+
 def test_autotune_toggle():
     prev = cb.conv2d_dgrad_set_autotune(False)
     assert cb.conv2d_dgrad_set_autotune(prev) is False
