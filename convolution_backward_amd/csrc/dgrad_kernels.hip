@@ -194,9 +194,20 @@ struct EpiTag {
     static constexpr int value = E;
 };
 
-template <int BM, int BN, int WM, int WN, bool SK>
+// Kernel variants by the work a launch carries (MODE): kPlain for GEMM tiles
+// alone, kZeroWork when zero phases ride along (zero stripes, standalone zero
+// chunks or companion stores), kStreamK for a split reduction (never with
+// zero work). Each drops the state the others need, which keeps the uniform
+// values of the main loop in scalar registers.
+constexpr int kPlain = 0;
+constexpr int kZeroWork = 1;
+constexpr int kStreamK = 2;
+
+template <int BM, int BN, int WM, int WN, int MODE>
 __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
 {
+    constexpr bool SK = MODE == kStreamK;
+    constexpr bool ZW = MODE == kZeroWork;
     constexpr int BK = 64;
     constexpr int NW = WM * WN;
     constexpr int NT = 64 * NW;
@@ -232,10 +243,10 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     const int ksteps = (K + BK - 1) / BK;
     const int SC = pin(a.S * C);          // filter elements per tap row
     const int RSC = pin(a.R * SC);        // filter elements per k
-    const uint32_t zps = SK ? 0u : pin((uint32_t)a.zps);
-    const uint32_t zt = SK ? 0u : pin((uint32_t)a.zt);
-    const uint32_t zabsorbed = SK ? 0u : pin(a.zabsorbed);
-    const int ncomp = SK ? 0 : pin(a.ncomp);
+    const uint32_t zps = ZW ? pin((uint32_t)a.zps) : 0u;
+    const uint32_t zt = ZW ? pin((uint32_t)a.zt) : 0u;
+    const uint32_t zabsorbed = ZW ? pin(a.zabsorbed) : 0u;
+    const int ncomp = ZW ? pin(a.ncomp) : 0;
 
     const __amdgpu_buffer_rsrc_t dx_rsrc = make_rsrc(a.dx, a.dx_bytes);
     const i32x4 dy_desc = raw_descriptor(a.dy, a.dy_bytes);
@@ -490,6 +501,8 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     // Exactly zps stores per request, so the waits below can count them;
     // those outside the tile's share are dropped by the range check.
     auto issue_zero = [&]() {
+        if constexpr (!ZW)
+            return;
         const uint32_t first = (uint32_t)(rq_niter - rq_left) * zps;
         for (uint32_t jz = 0; jz < zps; ++jz) {
             const uint32_t idx = first + jz;
@@ -783,7 +796,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             g = segment(round, t);
             if (!g.ok)
                 break;
-        } else {
+        } else if constexpr (ZW) {
             const int tile = round * G + slot;
             if (tile >= a.total_tiles)
                 break;
@@ -794,6 +807,12 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                     zero_stripe(first + u, first + u < a.zstripes);
                 continue;
             }
+            t = decode(tile);
+            g = Seg{tile, 0, t.niter, true};
+        } else {
+            const int tile = round * G + slot;
+            if (tile >= a.gemm_tiles)
+                break;
             t = decode(tile);
             g = Seg{tile, 0, t.niter, true};
         }
@@ -813,7 +832,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             // the first two slices after an epilogue, that epilogue's kEpiStores
             // stores (its z loads only make the wait stricter).
             if (inflight >= 2) {
-                if (zps != 0) {
+                if (ZW && zps != 0) {
                     if (post_epi > 0)
                         wait_vmcnt<LD + 2 * kMaxZeroPerSlice + kEpiStores>();
                     else
@@ -864,43 +883,51 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
 template <int BM, int BN, int WM, int WN>
 constexpr bool kHasStreamK = !(BM == 256 && BN == 64 && WM == 4);
 
+// The variant a launch needs (the host never asks 256x64/4x1 to split).
+inline int launch_mode(const KernelArgs& a)
+{
+    if (a.sk)
+        return kStreamK;
+    return (a.total_tiles > a.gemm_tiles || a.zstripes > 0 || a.ncomp > 0) ? kZeroWork : kPlain;
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch(const KernelArgs& a, hipStream_t stream)
 {
-    if constexpr (kHasStreamK<BM, BN, WM, WN>) {
-        if (a.sk) {
-            hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, true>), dim3(a.grid), dim3(64 * WM * WN), 0, stream, a);
+    const dim3 grid(a.grid), block(64 * WM * WN);
+    switch (launch_mode(a)) {
+    case kStreamK:
+        if constexpr (kHasStreamK<BM, BN, WM, WN>) {
+            hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, kStreamK>), grid, block, 0, stream, a);
             return hipGetLastError();
         }
-    } else {
-        if (a.sk)
-            return hipErrorInvalidValue;   // the host never plans this
+        return hipErrorInvalidValue;   // the host never plans this
+    case kZeroWork:
+        hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, kZeroWork>), grid, block, 0, stream, a);
+        return hipGetLastError();
+    default:
+        hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, kPlain>), grid, block, 0, stream, a);
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, false>), dim3(a.grid), dim3(64 * WM * WN), 0, stream, a);
-    return hipGetLastError();
 }
 
-// Resident workgroups of one configuration per CU on the current device.
+// Resident workgroups of one configuration per CU on the current device: the
+// fewest over its variants (a launch's grid assumes that many are resident).
 template <int BM, int BN, int WM, int WN>
 int resident(void)
 {
-    int n = 0;
-    // the stream-K instantiation must fit as many workgroups per CU (its
-    // ranges assume that many are resident); the smaller count of the two
-    int m = 1 << 20;
-    if constexpr (kHasStreamK<BM, BN, WM, WN>) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, true>),
-                                                         64 * WM * WN, 0) != hipSuccess) {
+    auto blocks = [](const void* f) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64 * WM * WN, 0) != hipSuccess) {
             (void)hipGetLastError();
-            return 1;
+            return 0;
         }
-    }
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, false>),
-                                                     64 * WM * WN, 0) != hipSuccess) {
-        (void)hipGetLastError();
-        return 1;
-    }
-    n = n < m ? n : m;
+        return n;
+    };
+    int n = std::min(blocks(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kPlain>)),
+                     blocks(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kZeroWork>)));
+    if constexpr (kHasStreamK<BM, BN, WM, WN>)
+        n = std::min(n, blocks(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kStreamK>)));
     return n > 0 ? n : 1;
 }
 
@@ -919,25 +946,26 @@ const TileConfig kConfigs[] = {CBW_TILE_CONFIGS(CBW_CONFIG_ENTRY)};
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs <= 64, "the launcher keeps per-config state for at most 64 configs");
 
-// Private (scratch) bytes per lane of one configuration's kernel, or -1 if
-// the runtime cannot tell.
+// Private (scratch) bytes per lane, summed over the configuration's variants,
+// or -1 if the runtime cannot tell.
 template <int BM, int BN, int WM, int WN>
 int private_bytes(void)
 {
-    hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, false>)) != hipSuccess) {
-        (void)hipGetLastError();
-        return -1;
-    }
-    size_t bytes = attr.localSizeBytes;
-    if constexpr (kHasStreamK<BM, BN, WM, WN>) {
-        if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, true>)) != hipSuccess) {
+    auto bytes = [](const void* f) -> long {
+        hipFuncAttributes attr;
+        if (hipFuncGetAttributes(&attr, f) != hipSuccess) {
             (void)hipGetLastError();
             return -1;
         }
-        bytes += attr.localSizeBytes;
-    }
-    return (int)bytes;
+        return (long)attr.localSizeBytes;
+    };
+    long b[3] = {bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kPlain>)),
+                 bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kZeroWork>)), 0};
+    if constexpr (kHasStreamK<BM, BN, WM, WN>)
+        b[2] = bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kStreamK>));
+    if (b[0] < 0 || b[1] < 0 || b[2] < 0)
+        return -1;
+    return (int)(b[0] + b[1] + b[2]);
 }
 
 using LaunchFn = hipError_t (*)(const KernelArgs&, hipStream_t);
