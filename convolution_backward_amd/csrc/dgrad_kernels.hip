@@ -84,6 +84,17 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferFlags);
 }
 
+// The kernel's arguments, read again from the kernarg segment where they are
+// used. The empty asm keeps the compiler from hoisting these loads, so that
+// values needed only now and then (the epilogue's descriptors) are not held
+// in scalar registers through the main loop.
+__device__ inline const __attribute__((address_space(4))) KernelArgs* kernargs()
+{
+    auto p = (const __attribute__((address_space(4))) KernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
 // The same descriptor as four dwords (base, stride 0, size, format), for the
 // inline-assembly loads.
 __device__ inline i32x4 raw_descriptor(const void* base, uint32_t bytes)
@@ -195,19 +206,22 @@ struct EpiTag {
 };
 
 // Kernel variants by the work a launch carries (MODE): kPlain for GEMM tiles
-// alone, kZeroWork when zero phases ride along (zero stripes, standalone zero
-// chunks or companion stores), kStreamK for a split reduction (never with
-// zero work). Each drops the state the others need, which keeps the uniform
-// values of the main loop in scalar registers.
+// alone, kCompanion when zero phases ride along only as companion stores,
+// kZeroWork for zero stripes and standalone zero chunks (and companions),
+// kStreamK for a split reduction (never with zero work). Each drops the state
+// the others need, which keeps the uniform values of the main loop in scalar
+// registers.
 constexpr int kPlain = 0;
 constexpr int kZeroWork = 1;
 constexpr int kStreamK = 2;
+constexpr int kCompanion = 3;
 
 template <int BM, int BN, int WM, int WN, int MODE>
 __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
 {
     constexpr bool SK = MODE == kStreamK;
-    constexpr bool ZW = MODE == kZeroWork;
+    constexpr bool ZW = MODE == kZeroWork;                 // zero stripes and chunks
+    constexpr bool CP = ZW || MODE == kCompanion;          // companion stores
     constexpr int BK = 64;
     constexpr int NW = WM * WN;
     constexpr int NT = 64 * NW;
@@ -246,7 +260,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     const uint32_t zps = ZW ? pin((uint32_t)a.zps) : 0u;
     const uint32_t zt = ZW ? pin((uint32_t)a.zt) : 0u;
     const uint32_t zabsorbed = ZW ? pin(a.zabsorbed) : 0u;
-    const int ncomp = ZW ? pin(a.ncomp) : 0;
+    const int ncomp = CP ? pin(a.ncomp) : 0;
 
     const __amdgpu_buffer_rsrc_t dx_rsrc = make_rsrc(a.dx, a.dx_bytes);
     const i32x4 dy_desc = raw_descriptor(a.dy, a.dy_bytes);
@@ -619,9 +633,11 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     static_assert(CH >= 2 && CH <= 64 && 64 % CH == 0, "whole pixel rows per store");
     constexpr int kEpiStores = FM * EST;     // stores of one epilogue (per wave)
     static_assert(LD + 2 * kMaxZeroPerSlice + kEpiStores < 64, "vmcnt range");
-    const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(a.epi != kEpiNone ? a.z : a.dx, a.dx_bytes);
     auto epilogue = [&](auto tag, const Tile& t, const PhaseArg& ph, int stage) {
         constexpr int E = decltype(tag)::value;
+        const auto* ka = kernargs();
+        const __amdgpu_buffer_rsrc_t e_dx = make_rsrc(ka->dx, ka->dx_bytes);
+        const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(E != kEpiNone ? ka->z : ka->dx, ka->dx_bytes);
         const int cw = t.c0 + wn * TN;    // first channel of this wave's block
         u32x2 zr[FM][FN][4];
         if constexpr (E != kEpiNone) {
@@ -676,10 +692,10 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                 const int c = cw + q * 8;
                 const uint32_t bad = (uint32_t)(m >= ph.M) | (uint32_t)(c >= C);
                 const uint32_t off = (pixel_offset(ph, m) + (uint32_t)c) * 2u;
-                __builtin_amdgcn_raw_buffer_store_b128(v, dx_rsrc, out_of_range_if(bad, off), 0, kStoreNT);
+                __builtin_amdgcn_raw_buffer_store_b128(v, e_dx, out_of_range_if(bad, off), 0, kStoreNT);
                 const u32x4 zero{0u, 0u, 0u, 0u};
                 for (int qc = 0; qc < ncomp; ++qc)   // companion zero pixels (same lattice point)
-                    __builtin_amdgcn_raw_buffer_store_b128(zero, dx_rsrc, out_of_range_if(bad, off + (uint32_t)a.comp_delta[qc] * 2u), 0, kStoreNT);
+                    __builtin_amdgcn_raw_buffer_store_b128(zero, e_dx, out_of_range_if(bad, off + (uint32_t)a.comp_delta[qc] * 2u), 0, kStoreNT);
             }
         }
     };
@@ -705,13 +721,15 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         const int seg = (int)((uint32_t)slot - first);
         const int nseg = (int)(sk_owner((uint32_t)(t.s0 + t.niter - 1)) - first) + 1;
         constexpr uint32_t kSegBytes = (uint32_t)BM * BN * 4;
+        const auto* ka = kernargs();
+        int* const count = ka->sk_count + tile;
         const __amdgpu_buffer_rsrc_t ws =
-            make_rsrc(a.sk_part + (size_t)tile * (size_t)a.sk_maxseg * (size_t)(BM * BN), (uint32_t)a.sk_maxseg * kSegBytes);
+            make_rsrc(ka->sk_part + (size_t)tile * (size_t)ka->sk_maxseg * (size_t)(BM * BN), (uint32_t)ka->sk_maxseg * kSegBytes);
         const uint32_t lane_off = (uint32_t)tid * 16u;
         __attribute__((address_space(3))) int* flag = (__attribute__((address_space(3))) int*)((lds_char*)lds + stage * STAGE);
         __syncthreads();                  // no wave reads the stage's operands any more
         if (tid == 0)
-            *flag = __hip_atomic_load(&a.sk_count[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nseg - 1 ? 1 : 0;
+            *flag = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nseg - 1 ? 1 : 0;
         __syncthreads();
         // one value for the whole workgroup: taken from the first lane so the
         // branches below are uniform in the compiler's eyes too
@@ -730,7 +748,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             wait_vmcnt<0>();              // this wave's partial sums are in memory
             __syncthreads();              // ... and every wave's; every wave has read the flag
             if (tid == 0) {
-                const int old = __hip_atomic_fetch_add(&a.sk_count[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int old = __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 *flag = old == nseg - 1 ? 1 : 0;
             }
             __syncthreads();
@@ -771,7 +789,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
             }
         }
         if (tid == 0)
-            __hip_atomic_store(&a.sk_count[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(count, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return true;
     };
 
@@ -888,7 +906,9 @@ inline int launch_mode(const KernelArgs& a)
 {
     if (a.sk)
         return kStreamK;
-    return (a.total_tiles > a.gemm_tiles || a.zstripes > 0 || a.ncomp > 0) ? kZeroWork : kPlain;
+    if (a.total_tiles > a.gemm_tiles || a.zstripes > 0)
+        return kZeroWork;
+    return a.ncomp > 0 ? kCompanion : kPlain;
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -904,6 +924,9 @@ hipError_t launch(const KernelArgs& a, hipStream_t stream)
         return hipErrorInvalidValue;   // the host never plans this
     case kZeroWork:
         hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, kZeroWork>), grid, block, 0, stream, a);
+        return hipGetLastError();
+    case kCompanion:
+        hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, kCompanion>), grid, block, 0, stream, a);
         return hipGetLastError();
     default:
         hipLaunchKernelGGL((dgrad_igemm<BM, BN, WM, WN, kPlain>), grid, block, 0, stream, a);
@@ -926,6 +949,7 @@ int resident(void)
     };
     int n = std::min(blocks(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kPlain>)),
                      blocks(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kZeroWork>)));
+    n = std::min(n, blocks(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kCompanion>)));
     if constexpr (kHasStreamK<BM, BN, WM, WN>)
         n = std::min(n, blocks(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kStreamK>)));
     return n > 0 ? n : 1;
@@ -959,13 +983,14 @@ int private_bytes(void)
         }
         return (long)attr.localSizeBytes;
     };
-    long b[3] = {bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kPlain>)),
-                 bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kZeroWork>)), 0};
+    long b[4] = {bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kPlain>)),
+                 bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kZeroWork>)),
+                 bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kCompanion>)), 0};
     if constexpr (kHasStreamK<BM, BN, WM, WN>)
-        b[2] = bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kStreamK>));
-    if (b[0] < 0 || b[1] < 0 || b[2] < 0)
+        b[3] = bytes(reinterpret_cast<const void*>(dgrad_igemm<BM, BN, WM, WN, kStreamK>));
+    if (b[0] < 0 || b[1] < 0 || b[2] < 0 || b[3] < 0)
         return -1;
-    return (int)(b[0] + b[1] + b[2]);
+    return (int)(b[0] + b[1] + b[2] + b[3]);
 }
 
 using LaunchFn = hipError_t (*)(const KernelArgs&, hipStream_t);
