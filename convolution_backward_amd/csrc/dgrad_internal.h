@@ -62,7 +62,9 @@ struct KernelArgs {
     int gemm_tiles;      // GEMM tiles over all phases with taps
     int total_tiles;     // GEMM tiles + zero chunks
     int grid;            // resident workgroups walking them (<= total_tiles)
-    int order;           // 0: channel tiles of a pixel block consecutive; 1: pixel blocks of a channel tile
+    int order;           // 0: channel tiles of a pixel block consecutive; 1: pixel blocks of a channel tile;
+                         // 2: the phases of a pixel block side by side (equal tile counts, grid % nphases == 0)
+                         //    with channel tiles next
     int xcd_mode;        // 0: rotating groups of `group` tiles per XCD; 1: contiguous eighths
     int group;           // consecutive tiles kept on one XCD (mode 0)
     int nphases;
@@ -109,6 +111,7 @@ struct TileConfig {
     const char* name;
     int lds_bytes;
     bool streamk;        // compiled with a stream-K variant
+    bool phase_order;    // supports tile order 2 (phases of a pixel block side by side)
 };
 
 int num_tile_configs();

@@ -205,6 +205,11 @@ struct EpiTag {
     static constexpr int value = E;
 };
 
+// The phase-interleaved tile order (order 2) exists for every configuration
+// but 256x64/4x1, whose scalar registers are full without it.
+template <int BM, int BN, int WM, int WN>
+constexpr bool kHasPhaseOrder = !(BM == 256 && BN == 64 && WM == 4);
+
 // Kernel variants by the work a launch carries (MODE): kPlain for GEMM tiles
 // alone, kCompanion when zero phases ride along only as companion stores,
 // kZeroWork for zero stripes and standalone zero chunks (and companions),
@@ -274,14 +279,27 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         int pi, m0, c0, niter, s0;   // s0: the tile's first slice in the launch's numbering
     };
     // GEMM tile `tile` (< gemm_tiles): its phase, first lattice row, first channel, slices.
-    auto decode = [&](int tile) -> Tile {
-        int pi = 0;
-        for (int i = 1; i < a.nphases; ++i)
-            if (tile >= a.ph[i].tile_begin)
-                pi = i;
-        const int local = tile - a.ph[pi].tile_begin;
+    // `round` is tile / G, which the walk knows.
+    auto decode = [&](int tile, int round) -> Tile {
+        int pi = 0, local = 0;
+        if (MODE == kPlain && kHasPhaseOrder<BM, BN, WM, WN> && kernargs()->order == 2) {   // the phases of one block side by
+            // side, rotating with the round (every phase has the same tiles and
+            // the grid is a multiple of the phase count, so this is a bijection
+            // onto phase-major numbers); launches of the plain variant only.
+            // Read in place: nothing of this is held through the main loop.
+            const int np = kernargs()->nphases;
+            const int blk = tile / np;
+            const int j = tile - blk * np;
+            pi = (j + round) % np;
+            local = blk;
+        } else {
+            for (int i = 1; i < a.nphases; ++i)
+                if (tile >= a.ph[i].tile_begin)
+                    pi = i;
+            local = tile - a.ph[pi].tile_begin;
+        }
         int tm, tn;
-        if (a.order == 0) {    // channel tiles of one pixel block are consecutive
+        if (a.order != 1) {    // channel tiles of one pixel block are consecutive
             tm = local / a.tiles_n;
             tn = local - tm * a.tiles_n;
         } else {               // pixel blocks of one channel tile are consecutive
@@ -321,7 +339,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
         const int tile = a.ph[pi].tile_begin + (int)((sk_s0 - (uint32_t)a.slice_begin[pi]) / (uint32_t)niter0) + k;
         if (tile >= a.gemm_tiles)
             return Seg{0, 0, 0, false};
-        t = decode(tile);
+        t = decode(tile, 0);
         const int lo = k == 0 ? (int)(sk_s0 - (uint32_t)t.s0) : 0;
         if ((uint32_t)(t.s0 + lo) >= sk_s1)
             return Seg{0, 0, 0, false};
@@ -432,7 +450,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                 const int tile = rq_round * G + slot;
                 if (tile >= a.gemm_tiles)
                     return false;
-                t = decode(tile);
+                t = decode(tile, rq_round);
                 g = Seg{tile, 0, t.niter, true};
             }
             ++rq_round;
@@ -825,13 +843,13 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                     zero_stripe(first + u, first + u < a.zstripes);
                 continue;
             }
-            t = decode(tile);
+            t = decode(tile, round);
             g = Seg{tile, 0, t.niter, true};
         } else {
             const int tile = round * G + slot;
             if (tile >= a.gemm_tiles)
                 break;
-            t = decode(tile);
+            t = decode(tile, round);
             g = Seg{tile, 0, t.niter, true};
         }
         const PhaseArg& ph = a.ph[t.pi];
@@ -965,7 +983,8 @@ int resident(void)
     X(128, 256, 2, 4)
 
 #define CBW_CONFIG_ENTRY(BM, BN, WM, WN) \
-    {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN, 3 * (BM + BN) * 64 * 2, kHasStreamK<BM, BN, WM, WN>},
+    {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN, 3 * (BM + BN) * 64 * 2, kHasStreamK<BM, BN, WM, WN>, \
+     kHasPhaseOrder<BM, BN, WM, WN>},
 const TileConfig kConfigs[] = {CBW_TILE_CONFIGS(CBW_CONFIG_ENTRY)};
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs <= 64, "the launcher keeps per-config state for at most 64 configs");

@@ -126,11 +126,14 @@ def _bits_equal(gpu, ref16):
 
 
 @pytest.mark.parametrize("shape", [(2, 12, 12, 64, 64, 3, 3, 1, 1), (2, 13, 14, 72, 64, 3, 3, 2, 1),
-                                   (1, 9, 9, 16, 136, 1, 1, 2, 0), (1, 10, 11, 24, 40, 5, 3, 3, 2)],
+                                   (1, 9, 9, 16, 136, 1, 1, 2, 0), (1, 10, 11, 24, 40, 5, 3, 3, 2),
+                                   (2, 16, 18, 72, 64, 3, 3, 2, 1), (2, 18, 18, 16, 24, 3, 3, 3, 1)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_integer_inputs_bit_exact(shape):
     """Integer dy, w in [-8, 8]: every partial sum is an exact fp32 integer,
-    and sums above 2048 exercise fp16 round-to-nearest-even."""
+    and sums above 2048 exercise fp16 round-to-nearest-even. The last two
+    shapes have 4 and 9 phases of equal lattice size, whose tiles run in the
+    phase-interleaved order."""
     cfg = _cfg(shape)
     inp = integer_inputs(cfg, lo=-8, hi=8, seed=21)
     ref16 = oracle.round_to_half(ref_full(cfg, inp))
