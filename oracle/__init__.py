@@ -1,4 +1,4 @@
-"""ctypes front end of the fp64 CPU oracle for conv2d dgrad.
+"""ctypes front end of the fp64 CPU oracle for conv2d dgrad (and wgrad).
 
 TEST INFRASTRUCTURE: only tests/, ``__graft_entry__.smoke()`` and the CPU
 baseline leg of ``bench.py`` may import this package. The product package
@@ -57,6 +57,8 @@ def _bind(lib):
     lib.oracle_dgrad_rows.restype = i
     lib.oracle_dgrad_full.argtypes = [u16p, u16p, u16p] + [i] * 10 + [f64p, i]
     lib.oracle_dgrad_full.restype = i
+    lib.oracle_wgrad_rows.argtypes = [u16p, u16p] + [i] * 9 + [i64p, ctypes.c_int64, f64p, f64p, i]
+    lib.oracle_wgrad_rows.restype = i
     lib.oracle_round_to_half.argtypes = [f64p, u16p, ctypes.c_int64]
     lib.oracle_round_to_half.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -124,6 +126,39 @@ def dgrad(dy, w, H, W, stride, pad, epilogue=EPI_NONE, z=None, rows=None,
         raise ValueError(f"oracle_dgrad failed with code {rc}")
     del dyk, wk, zk
     return out
+
+
+def wgrad(dy, x, R, S, stride, pad, rows=None, with_abs=False, threads=0, lib=None):
+    """fp64 filter gradient of float16 dy [N,P,Q,K] and x [N,H,W,C].
+
+    Returns [K,R,S,C] float64, or [len(rows), C] when ``rows`` (linear filter
+    rows (k*R + r)*S + t) is given. With ``with_abs`` also returns the sums of
+    |dy * x| of the same shape.
+    """
+    lib = lib or load()
+    N, P, Q, K = dy.shape
+    N2, H, W, C = x.shape
+    if N2 != N:
+        raise ValueError("dy and x disagree on N")
+    if (lib.oracle_out_extent(H, R, stride, pad), lib.oracle_out_extent(W, S, stride, pad)) != (P, Q):
+        raise ValueError("dy spatial shape does not match H, W, R, S, stride, pad")
+    dyk, dyp = _u16(dy)
+    xk, xp = _u16(x)
+    rr = np.arange(K * R * S, dtype=np.int64) if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.empty((len(rr), C), dtype=np.float64)
+    mag = np.empty((len(rr), C), dtype=np.float64) if with_abs else None
+    f64p = ctypes.POINTER(ctypes.c_double)
+    rc = lib.oracle_wgrad_rows(dyp, xp, N, H, W, C, K, R, S, stride, pad,
+                               rr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(rr),
+                               out.ctypes.data_as(f64p), mag.ctypes.data_as(f64p) if with_abs else None,
+                               int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_wgrad failed with code {rc}")
+    del dyk, xk
+    if rows is None:
+        out = out.reshape(K, R, S, C)
+        mag = mag.reshape(K, R, S, C) if with_abs else None
+    return (out, mag) if with_abs else out
 
 
 def round_to_half(x, lib=None) -> np.ndarray:

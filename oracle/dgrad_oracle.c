@@ -36,6 +36,8 @@
  *
  * Layouts: dy [N][P][Q][K], w [K][R][S][C], z and dx [N][H][W][C], all
  * C-contiguous. Output rows are linear pixel indices (n*H + h)*W + w.
+ *
+ * The file also holds the filter gradient (wgrad) of the same layer, below.
  */
 #include <math.h>
 #include <stdint.h>
@@ -269,6 +271,95 @@ int oracle_dgrad_full(const uint16_t* dy, const uint16_t* wt, const uint16_t* z,
                                rows, npix, out, nthreads);
     free(rows);
     return rc;
+}
+
+/* ---- wgrad, one filter row at a time ------------------------------------ */
+
+/*
+ * The gradient of the same forward layer with respect to its filter (the
+ * "wgrad" that "[CUTLASS] Conv2d dgrad", apache/tvm PR #10110, defers):
+ *   dw[k,r,t,c] = sum over n,p,q of dy[n,p,q,k] * x[n, p*s - pad + r, q*s - pad + t, c],
+ * where an input position outside the image (padding) contributes zero.
+ *
+ * For each requested filter row (k,r,t): walk every dy position (n,p,q),
+ * keep it when the input position is inside the image, and accumulate
+ * dy[n,p,q,k] * x[n,h,w,c] over all c. When abs_out is not NULL it receives
+ * the sum of |dy * x| (the scale of the rounding error a float sum can make).
+ *
+ * rows: linear filter-row indices (k*R + r)*S + t; out, abs_out: [nrows][C].
+ * Returns 0 on success, 1 on invalid arguments, 2 on allocation failure.
+ */
+int oracle_wgrad_rows(const uint16_t* dy, const uint16_t* x,
+                      int N, int H, int W, int C, int K, int R, int S,
+                      int stride, int pad,
+                      const int64_t* rows, int64_t nrows, double* out, double* abs_out, int nthreads)
+{
+    if (check_args(N, H, W, C, K, R, S, stride, pad, ORACLE_EPI_NONE, NULL))
+        return 1;
+    if (nrows < 0 || (nrows > 0 && (rows == NULL || out == NULL)) || dy == NULL || x == NULL)
+        return 1;
+    const int P = oracle_out_extent(H, R, stride, pad);
+    const int Q = oracle_out_extent(W, S, stride, pad);
+    const int64_t nfrows = (int64_t)K * R * S;
+    for (int64_t i = 0; i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= nfrows)
+            return 1;
+    double* lut = (double*)malloc(sizeof(double) * 65536);
+    if (!lut)
+        return 2;
+    for (int b = 0; b < 65536; ++b)
+        lut[b] = oracle_half_to_double((uint16_t)b);
+    if (nthreads < 1)
+        nthreads = omp_get_max_threads();
+    int failed = 0;
+
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* acc = (double*)malloc(sizeof(double) * (size_t)C * 2);
+        if (!acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < nrows; ++it) {
+            if (!acc)
+                continue;
+            const int64_t fr = rows[it];
+            const int k = (int)(fr / ((int64_t)R * S));
+            const int r = (int)((fr / S) % R);
+            const int t = (int)(fr % S);
+            double* sum = acc;
+            double* mag = acc + C;
+            for (int c = 0; c < C; ++c)
+                sum[c] = mag[c] = 0.0;
+            for (int n = 0; n < N; ++n)
+                for (int p = 0; p < P; ++p) {
+                    const int h = p * stride - pad + r;
+                    if (h < 0 || h >= H)
+                        continue;
+                    for (int q = 0; q < Q; ++q) {
+                        const int w = q * stride - pad + t;
+                        if (w < 0 || w >= W)
+                            continue;
+                        const double d = lut[dy[(((int64_t)n * P + p) * Q + q) * K + k]];
+                        const uint16_t* xrow = x + (((int64_t)n * H + h) * W + w) * C;
+                        for (int c = 0; c < C; ++c) {
+                            const double v = d * lut[xrow[c]];
+                            sum[c] += v;
+                            mag[c] += fabs(v);
+                        }
+                    }
+                }
+            for (int c = 0; c < C; ++c) {
+                out[it * (int64_t)C + c] = sum[c];
+                if (abs_out)
+                    abs_out[it * (int64_t)C + c] = mag[c];
+            }
+        }
+        free(acc);
+    }
+    free(lut);
+    return failed ? 2 : 0;
 }
 
 /* RNE fp16 encoding of an fp64 array (bit-exact comparisons). */

@@ -347,11 +347,137 @@ def check_rows_api(lib):
     assert np.array_equal(part, full[rows])
 
 
+# ----------------------------------------------------------------- wgrad pins
+
+
+def check_wgrad_hand_examples(lib):
+    """Single channel, x = W9 = [[1,2,3],[4,5,6],[7,8,9]], worked by hand.
+
+    (a) 3x3 filter, stride 1, no padding: P = Q = 1, so dw[r,t] = dy * x[r,t];
+        with dy = 1 that is W9 itself.
+    (b) 3x3 filter, stride 1, padding 1, dy = all ones (3x3): dw[r,t] sums x
+        over the rows h = p - 1 + r and columns w = q - 1 + t that stay inside.
+        r = 0 keeps rows 0-1, r = 1 all rows, r = 2 rows 1-2 (columns alike):
+        [[1+2+4+5, 1+2+3+4+5+6, 2+3+5+6],
+         [1+2+4+5+7+8, 45, 2+3+5+6+8+9],
+         [4+5+7+8, 4+5+6+7+8+9, 5+6+8+9]] = [[12,21,16],[27,45,33],[24,39,28]].
+    (c) 1x1 filter, stride 2, no padding: P = Q = 2 at x[0,0], x[0,2], x[2,0],
+        x[2,2] = 1, 3, 7, 9; with dy = [[1,2],[3,4]], dw = 1 + 6 + 21 + 36 = 64.
+    """
+    x = f16(W9.reshape(1, 3, 3, 1))
+    got = oracle.wgrad(f16(np.ones((1, 1, 1, 1))), x, 3, 3, 1, 0, lib=lib)
+    assert np.array_equal(got.reshape(3, 3), W9)
+    got = oracle.wgrad(f16(np.ones((1, 3, 3, 1))), x, 3, 3, 1, 1, lib=lib)
+    assert np.array_equal(got.reshape(3, 3), np.array([[12, 21, 16], [27, 45, 33], [24, 39, 28]], float))
+    got = oracle.wgrad(f16(np.array([[1, 2], [3, 4]]).reshape(1, 2, 2, 1)), x, 1, 1, 2, 0, lib=lib)
+    assert got.reshape(()) == 64.0
+
+
+WGRAD_CASES = [(2, 7, 6, 3, 4, 3, 3, 2, 1), (1, 8, 8, 2, 3, 3, 3, 1, 1), (2, 6, 7, 4, 2, 1, 1, 2, 0),
+               (1, 9, 8, 3, 2, 5, 3, 3, 2), (1, 5, 5, 2, 2, 2, 4, 1, 0), (2, 10, 9, 2, 3, 3, 3, 2, 0)]
+
+
+def _wgrad_inputs(rng, N, H, W, C, K, R, S, s, pad):
+    P, Q = _ext(H, R, s, pad), _ext(W, S, s, pad)
+    return f16(rng.standard_normal((N, P, Q, K))), f16(rng.standard_normal((N, H, W, C)))
+
+
+def check_wgrad_adjoint_forward(lib):
+    """<wgrad(dy, x), w> = <dy, forward(x, w)> for any w: wgrad is the
+    adjoint of the map w -> forward(x, w); the forward here slices a padded x."""
+    rng = np.random.Generator(np.random.PCG64(30))
+    for (N, H, W, C, K, R, S, s, pad) in WGRAD_CASES:
+        dy, x = _wgrad_inputs(rng, N, H, W, C, K, R, S, s, pad)
+        w = rng.standard_normal((K, R, S, C))
+        lhs = np.sum(oracle.wgrad(dy, x, R, S, s, pad, lib=lib) * w)
+        rhs = np.sum(forward_conv(x, w, s, pad) * dy.astype(np.float64))
+        assert np.isclose(lhs, rhs, rtol=1e-11, atol=1e-11)
+
+
+def check_wgrad_adjoint_dgrad(lib):
+    """<wgrad(dy, x), w> = <dy, forward(x, w)> = <dgrad(dy, w), x>: the two
+    gradients of one layer are tied through its forward."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    for (N, H, W, C, K, R, S, s, pad) in WGRAD_CASES:
+        dy, x = _wgrad_inputs(rng, N, H, W, C, K, R, S, s, pad)
+        w = f16(rng.standard_normal((K, R, S, C)))
+        lhs = np.sum(oracle.wgrad(dy, x, R, S, s, pad, lib=lib) * w.astype(np.float64))
+        rhs = np.sum(oracle.dgrad(dy, w, H, W, s, pad, lib=lib) * x.astype(np.float64))
+        assert np.isclose(lhs, rhs, rtol=1e-11, atol=1e-11)
+
+
+def check_wgrad_unit_vectors(lib):
+    """Build the map w -> forward(x, w) column by column from unit filters;
+    wgrad(dy, x) must be its transpose applied to dy."""
+    rng = np.random.Generator(np.random.PCG64(32))
+    for (N, H, W, C, K, R, S, s, pad) in [(1, 5, 4, 2, 2, 3, 3, 2, 1), (2, 4, 5, 1, 3, 2, 3, 1, 0)]:
+        dy, x = _wgrad_inputs(rng, N, H, W, C, K, R, S, s, pad)
+        nw = K * R * S * C
+        A = np.zeros((dy.size, nw))
+        for i in range(nw):
+            e = np.zeros(nw)
+            e[i] = 1.0
+            A[:, i] = forward_conv(x, e.reshape(K, R, S, C), s, pad).ravel()
+        ref = (A.T @ dy.astype(np.float64).ravel()).reshape(K, R, S, C)
+        assert np.allclose(oracle.wgrad(dy, x, R, S, s, pad, lib=lib), ref, rtol=1e-12, atol=1e-12)
+
+
+def check_wgrad_matmul_special_cases(lib):
+    """1x1 filters: stride 1 is dy[M,K]^T @ x[M,C]; stride s reads x on the
+    (s*p, s*q) lattice only."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    N, H, W, C, K = 2, 5, 6, 7, 9
+    dy = f16(rng.standard_normal((N, H, W, K)))
+    x = f16(rng.standard_normal((N, H, W, C)))
+    got = oracle.wgrad(dy, x, 1, 1, 1, 0, lib=lib).reshape(K, C)
+    ref = dy.astype(np.float64).reshape(-1, K).T @ x.astype(np.float64).reshape(-1, C)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    for s, H, W in [(2, 7, 8), (3, 7, 9)]:
+        P, Q = _ext(H, 1, s, 0), _ext(W, 1, s, 0)
+        dy = f16(rng.standard_normal((N, P, Q, K)))
+        x = f16(rng.standard_normal((N, H, W, C)))
+        got = oracle.wgrad(dy, x, 1, 1, s, 0, lib=lib).reshape(K, C)
+        ref = dy.astype(np.float64).reshape(-1, K).T @ x.astype(np.float64)[:, ::s, ::s, :][:, :P, :Q, :].reshape(-1, C)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_wgrad_torch_conv2d_weight(lib):
+    """Cross-check with PyTorch's CPU fp64 conv2d weight gradient (NCHW)."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(34))
+    for (N, H, W, C, K, R, S, s, pad) in WGRAD_CASES:
+        dy, x = _wgrad_inputs(rng, N, H, W, C, K, R, S, s, pad)
+        ref = torch.nn.grad.conv2d_weight(
+            torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2).contiguous(), (K, C, R, S),
+            torch.from_numpy(dy.astype(np.float64)).permute(0, 3, 1, 2).contiguous(),
+            stride=s, padding=pad).permute(0, 2, 3, 1).numpy()
+        got = oracle.wgrad(dy, x, R, S, s, pad, lib=lib)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_wgrad_rows_and_abs(lib):
+    """Sampled filter rows equal the full result's rows, and the magnitude
+    sums equal wgrad of |dy| and |x| (|d * v| = |d| * |v|)."""
+    rng = np.random.Generator(np.random.PCG64(35))
+    N, H, W, C, K, R, S, s, pad = 2, 7, 6, 5, 4, 3, 3, 2, 1
+    dy, x = _wgrad_inputs(rng, N, H, W, C, K, R, S, s, pad)
+    full, mag = oracle.wgrad(dy, x, R, S, s, pad, with_abs=True, lib=lib)
+    rows = rng.choice(K * R * S, size=12, replace=False)
+    part = oracle.wgrad(dy, x, R, S, s, pad, rows=rows, lib=lib)
+    assert np.array_equal(part, full.reshape(-1, C)[rows])
+    ref = oracle.wgrad(np.abs(dy), np.abs(x), R, S, s, pad, lib=lib)
+    assert np.allclose(mag, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(mag >= np.abs(full) - 1e-12)
+
+
 ALL_CHECKS = [
     check_fp16_decode, check_fp16_rne_encode, check_out_extent, check_hand_examples,
     check_scatter_bruteforce, check_adjoint_identity, check_adjoint_unit_vectors,
     check_matmul_special_cases, check_stride1_flipped_forward, check_torch_conv2d_input,
     check_epilogue_factors, check_epilogue_applied, check_rows_api,
+    check_wgrad_hand_examples, check_wgrad_adjoint_forward, check_wgrad_adjoint_dgrad,
+    check_wgrad_unit_vectors, check_wgrad_matmul_special_cases, check_wgrad_torch_conv2d_weight,
+    check_wgrad_rows_and_abs,
 ]
 
 

@@ -33,6 +33,13 @@ MUTANTS = {
     "rounding_truncates": ("nearbyint(a / quantum)", "floor(a / quantum)"),
     "epilogue_skipped": ("o[c] = acc[c] * epilogue_factor(epi, lut[zrow[c]]);", "o[c] = acc[c];"),
     "pad_used_once": ("const int b = x + pad - t;", "const int b = x - t;"),
+    "wgrad_pad_sign": ("const int h = p * stride - pad + r;", "const int h = p * stride + pad - r;"),
+    "wgrad_column_bound": ("if (w < 0 || w >= W)", "if (w < 0 || w > W)"),
+    "wgrad_filter_row_decode": ("const int r = (int)((fr / S) % R);\n            const int t = (int)(fr % S);",
+                                "const int t = (int)((fr / R) % S);\n            const int r = (int)(fr % R);"),
+    "wgrad_input_transposed": ("x + (((int64_t)n * H + h) * W + w) * C", "x + (((int64_t)n * W + w) * H + h) * C"),
+    "wgrad_signed_magnitude": ("mag[c] += fabs(v);", "mag[c] += v;"),
+    "wgrad_stride_ignored": ("const int w = q * stride - pad + t;", "const int w = q - pad + t;"),
 }
 
 _CHILD = r"""
