@@ -27,7 +27,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import CONFIGS, EPI_NAMES, make_inputs  # noqa: E402
+from workloads import CONFIGS, EPI_NAMES, make_inputs, make_x  # noqa: E402
 
 SUITE = [1, 2, 3, 4, 5]            # indices into CONFIGS; 0 is the latency-sized parity case
 MFMA_PEAK_TFLOPS = 2500.0          # MI355X dense fp16 matrix-core peak
@@ -109,6 +109,8 @@ def main():
                     help="share of each layer's pixels the oracle computes for cpu_baseline (0 skips it)")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="cold-cache launches per layer, each after a 512 MiB scratch write (0 skips)")
+    ap.add_argument("--wgrad-reps", type=int, default=10,
+                    help="timed wgrad (filter gradient) calls per layer, after the dgrad timing (0 skips)")
     ap.add_argument("--only", default="",
                     help="comma-separated layer names: time only these (for profiler runs)")
     ap.add_argument("--copy-calibrate-mb", type=float, default=0.0,
@@ -234,6 +236,49 @@ def main():
                 "value": sum(cfg.useful_flops() for cfg, _ in layers) / cold_s / 1e12, "unit": "TFLOP/s",
                 "layers": cold_layers}
 
+    # ---- wgrad (the filter gradient, a NEXT row of the same layer): each
+    # layer's dy with a seeded x, automatic tile config and split count,
+    # HIP events around each call (its two kernels); not part of `value`
+    wgrad = None
+    if args.wgrad_reps > 0:
+        wlayers = []
+        for cfg, d in layers:
+            x = torch.from_numpy(make_x(cfg)).to(dev)
+            dw = torch.empty((cfg.K, cfg.R, cfg.S, cfg.C), dtype=torch.float32, device=dev)
+
+            def wcall():
+                cb.conv2d_wgrad_nhwc(d["dy"], x, dw, cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
+                                     cfg.stride, cfg.pad, stream.cuda_stream)
+            for _ in range(3):
+                wcall()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.wgrad_reps)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                wcall()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+            avg = float(np.mean(ms))
+            fl = cfg.useful_flops()
+            nbytes = 2 * (cfg.N * cfg.P * cfg.Q * cfg.K + cfg.N * cfg.H * cfg.W * cfg.C) + 4 * cfg.K * cfg.R * cfg.S * cfg.C
+            ai = fl / nbytes
+            if ai >= RIDGE:
+                rl = {"bound": "mfma", "achieved": fl / (avg * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
+            else:
+                rl = {"bound": "hbm", "achieved": nbytes / (avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+            rl["frac"] = rl["achieved"] / rl["peak"]
+            wlayers.append({"layer": cfg.name, "avg_us": avg * 1e3, "min_us": float(np.min(ms)) * 1e3,
+                            "tflops": fl / (avg * 1e-3) / 1e12, "alg_mb": nbytes / 1e6, "roofline": rl})
+            log(f"[wgrad] {cfg.name:34s} {avg*1e3:9.2f} us  {wlayers[-1]['tflops']:7.1f} TFLOP/s  "
+                f"{rl['bound']} {rl['frac']:.1%}")
+            del x, dw
+        wsum = sum(w["avg_us"] for w in wlayers) * 1e-6
+        wgrad = {"note": "dw[k,r,s,c] = sum dy*x (fp32 out), x = max(N(0,1),0) seeded; split-K GEMM plus an "
+                         "ordered reduction kernel; suite value = useful FLOPs / sum of per-layer means",
+                 "value": sum(cfg.useful_flops() for cfg, _ in layers) / wsum / 1e12, "unit": "TFLOP/s",
+                 "layers": wlayers}
+
     flops = sum(cfg.useful_flops() for cfg, _ in layers)
     kernel_ms = sum(p["avg_us"] for p in per_layer) / 1e3
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -275,6 +320,7 @@ def main():
         "cpu_baseline": cpu,
         "layers": per_layer,
         "cold": cold,
+        "wgrad": wgrad,
         "device": torch.cuda.get_device_name(dev),
         "build": cb.conv2d_dgrad_build_info(),
     }

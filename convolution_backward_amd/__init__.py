@@ -58,6 +58,10 @@ def _bind(lib):
     lib.conv2d_dgrad_cache_load.argtypes = [ctypes.c_char_p]
     lib.conv2d_dgrad_plan.argtypes = [i] * 9 + [ctypes.POINTER(_Phase), i, ip, ip, ip]
     lib.conv2d_dgrad_check.argtypes = [vp, vp, vp] + [i] * 10 + [vp]
+    lib.conv2d_wgrad_nhwc.argtypes = [vp, vp, vp] + [i] * 9 + [vp]
+    lib.conv2d_wgrad_nhwc_config.argtypes = [vp, vp, vp] + [i] * 9 + [i, i, vp]
+    lib.conv2d_wgrad_num_configs.argtypes = []
+    lib.conv2d_wgrad_check.argtypes = [vp, vp, vp] + [i] * 9
     lib.conv2d_dgrad_last_error.argtypes = []
     lib.conv2d_dgrad_last_error.restype = ctypes.c_char_p
     lib.conv2d_dgrad_build_info.argtypes = []
@@ -65,7 +69,8 @@ def _bind(lib):
     for name in ("conv2d_dgrad_nhwc", "conv2d_dgrad_nhwc_config", "conv2d_dgrad_num_configs",
                  "conv2d_dgrad_config_name", "conv2d_dgrad_query_config", "conv2d_dgrad_set_autotune",
                  "conv2d_dgrad_set_streamk", "conv2d_dgrad_streamk_launches", "conv2d_dgrad_cache_clear", "conv2d_dgrad_cache_size", "conv2d_dgrad_cache_save",
-                 "conv2d_dgrad_cache_load", "conv2d_dgrad_plan", "conv2d_dgrad_check"):
+                 "conv2d_dgrad_cache_load", "conv2d_dgrad_plan", "conv2d_dgrad_check",
+                 "conv2d_wgrad_nhwc", "conv2d_wgrad_nhwc_config", "conv2d_wgrad_num_configs", "conv2d_wgrad_check"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -132,6 +137,48 @@ def conv2d_dgrad_check(dy, w, dx, N, H, W, C, K, R, S, stride, pad, epilogue=EPI
     """Validation only: the status code, no exception, no HIP call."""
     return get_lib().conv2d_dgrad_check(_ptr(dy), _ptr(w), _ptr(dx), N, H, W, C, K, R, S, stride, pad,
                                         epilogue, _ptr(z))
+
+
+def conv2d_wgrad_nhwc(dy, x, dw, N, H, W, C, K, R, S, stride, pad, stream=None):
+    """dw (fp32 [K,R,S,C]) = wgrad(dy, x), enqueued on `stream` (default: torch's current stream)."""
+    return _check(get_lib().conv2d_wgrad_nhwc(_ptr(dy), _ptr(x), _ptr(dw), N, H, W, C, K, R, S, stride, pad,
+                                              _stream(stream, dy, dw)))
+
+
+def conv2d_wgrad_nhwc_config(dy, x, dw, N, H, W, C, K, R, S, stride, pad, config_id=0, splits=0, stream=None):
+    return _check(get_lib().conv2d_wgrad_nhwc_config(_ptr(dy), _ptr(x), _ptr(dw), N, H, W, C, K, R, S, stride,
+                                                     pad, config_id, splits, _stream(stream, dy, dw)))
+
+
+def conv2d_wgrad_check(dy, x, dw, N, H, W, C, K, R, S, stride, pad) -> int:
+    """Validation only: the status code, no exception, no HIP call."""
+    return get_lib().conv2d_wgrad_check(_ptr(dy), _ptr(x), _ptr(dw), N, H, W, C, K, R, S, stride, pad)
+
+
+def conv2d_wgrad_num_configs() -> int:
+    return get_lib().conv2d_wgrad_num_configs()
+
+
+def wgrad(dy, x, R, S, stride, pad, config_id=None, splits=0, out=None):
+    """Allocate dw [K,R,S,C] float32 with torch.empty and fill it on the current stream.
+
+    dy [N,P,Q,K] and x [N,H,W,C] are float16 GPU tensors.
+    """
+    import torch
+    for name, t in (("dy", dy), ("x", x)):
+        if t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
+    N, _, _, K = dy.shape
+    N2, H, W, C = x.shape
+    if N2 != N:
+        raise ValueError("dy and x disagree on N")
+    dw = out if out is not None else torch.empty((K, R, S, C), dtype=torch.float32, device=dy.device)
+    if config_id is None and splits == 0:
+        conv2d_wgrad_nhwc(dy, x, dw, N, H, W, C, K, R, S, stride, pad)
+    else:
+        conv2d_wgrad_nhwc_config(dy, x, dw, N, H, W, C, K, R, S, stride, pad,
+                                 0 if config_id is None else config_id, splits)
+    return dw
 
 
 def conv2d_dgrad_num_configs() -> int:
@@ -234,5 +281,6 @@ __all__ = [
     "conv2d_dgrad_set_streamk", "conv2d_dgrad_streamk_launches",
     "conv2d_dgrad_cache_clear", "conv2d_dgrad_cache_size", "conv2d_dgrad_cache_save", "conv2d_dgrad_cache_load",
     "conv2d_dgrad_plan", "conv2d_dgrad_last_error", "conv2d_dgrad_build_info", "dgrad", "get_lib",
+    "conv2d_wgrad_nhwc", "conv2d_wgrad_nhwc_config", "conv2d_wgrad_check", "conv2d_wgrad_num_configs", "wgrad",
     "DgradError", "EPI_NONE", "EPI_DRELU", "EPI_DHARDSWISH",
 ]

@@ -114,6 +114,40 @@ struct TileConfig {
     bool phase_order;    // supports tile order 2 (phases of a pixel block side by side)
 };
 
+// ------------------------------------------------------------------ wgrad
+
+// Filter gradient of the same layer (see wgrad_igemm in dgrad_kernels.hip):
+// dw[k,r,t,c] = sum over pixels m = (n,p,q) of dy[m,k] * x[n, p*s-pad+r, q*s-pad+t, c].
+// One GEMM per tap, D[c][k] = sum_m x_tap[m][c] * dy[m][k], over tiles of BC
+// channels x BK output channels; the pixel reduction (64-pixel slices) is cut
+// into `splits` contiguous ranges whose fp32 partial sums a second kernel adds
+// in split order.
+struct WgradArgs {
+    const uint16_t* dy;
+    const uint16_t* x;
+    float* dw;           // [K][R][S][C] fp32, fully written
+    float* part;         // [splits][tiles][BC*BK] fp32 partial sums in register order
+    uint32_t dy_bytes;
+    uint32_t x_bytes;
+    int N, H, W, C, K, R, S, P, Q, stride, pad;
+    int npq;             // N*P*Q: reduction length
+    int slices;          // ceil(npq / 64)
+    int tiles_c, tiles_k, tiles;   // tiles = R*S*tiles_c*tiles_k (tap outermost, output channels fastest)
+    int splits;
+    FastDiv div_pq;      // division by P*Q
+    FastDiv div_q;       // division by Q
+};
+
+struct WgradConfig {
+    int BC, BK, WC, WK;
+    const char* name;
+};
+int wgrad_num_configs();
+const WgradConfig& wgrad_config(int id);
+hipError_t launch_wgrad(int id, const WgradArgs& a, hipStream_t stream);
+hipError_t launch_wgrad_reduce(int id, const WgradArgs& a, hipStream_t stream);
+int wgrad_private_bytes(int id);   // scratch bytes per lane of both kernels, -1 if unknown
+
 int num_tile_configs();
 const TileConfig& tile_config(int id);
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);

@@ -1044,4 +1044,313 @@ hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream)
     return kLaunch[id](a, stream);
 }
 
+// ===================================================================== wgrad
+//
+// The filter gradient of the same layer,
+//   dw[k,r,t,c] = sum over pixels m = (n,p,q) of dy[m,k] * x[n, p*s-pad+r, q*s-pad+t, c],
+// as one GEMM per tap (r,t): D[c][k] = sum_m x_tap[m][c] * dy[m][k], with A =
+// x_tap^T (rows = channels c) and B = dy (columns = output channels k). The
+// reduction runs over the N*P*Q pixels in slices of 64; both slices are
+// [64 pixels][channels] tiles in LDS, loaded row by row straight from HBM
+// like the dgrad filter slice, and both fragments (8 consecutive pixels of
+// one channel) come from transpose reads. A launch covers tiles x splits
+// workgroups: workgroup b runs tile b mod tiles over the b / tiles-th of the
+// launch's contiguous slice ranges, and writes its fp32 accumulators to the
+// partial buffer in register order; a second kernel adds the splits in order.
+
+namespace {
+
+template <int BC, int BK, int WC, int WK>
+__global__ void __launch_bounds__(64 * WC * WK) wgrad_igemm(WgradArgs a)
+{
+    constexpr int BR = 64;                        // pixels per slice
+    constexpr int NW = WC * WK;
+    constexpr int NT = 64 * NW;
+    constexpr int TC = BC / WC, TK = BK / WK;     // wave tile: TC channels x TK output channels
+    constexpr int FN = TC / 32, FM = TK / 32;
+    constexpr int XROW = BC * 2, DROW = BK * 2;   // bytes of one pixel row of each slice
+    constexpr int X_BYTES = BR * XROW, D_BYTES = BR * DROW;
+    constexpr int STAGE = X_BYTES + D_BYTES;
+    constexpr int X_INSTR = X_BYTES / 1024 / NW, D_INSTR = D_BYTES / 1024 / NW;
+    constexpr int LD = X_INSTR + D_INSTR;         // loads per lane per slice
+    constexpr int XCH = XROW / 16, DCH = DROW / 16;   // 16-byte chunks per row
+    static_assert(TC % 32 == 0 && TK % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(X_BYTES % (1024 * NW) == 0 && D_BYTES % (1024 * NW) == 0, "whole 1 KiB blocks per wave");
+    static_assert(XROW % 256 == 0 && DROW % 256 == 0, "rows of whole bank windows");
+    static_assert(3 * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(2 * LD < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) char lds[3 * STAGE];
+    const uint32_t lds_u32 = (uint32_t)(uintptr_t)((lds_char*)lds);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wc = wave % WC;
+    const int wk = wave / WC;
+
+    const int tiles = pin(a.tiles);
+    const int tile = pin((int)(blockIdx.x % (uint32_t)tiles));
+    const int split = pin((int)(blockIdx.x / (uint32_t)tiles));
+    const int kb = tile % a.tiles_k;
+    const int rest = tile / a.tiles_k;
+    const int cb = rest % a.tiles_c;
+    const int tap = rest / a.tiles_c;
+    const int r = tap / a.S;
+    const int t = tap - r * a.S;
+    const int c0 = pin(cb * BC);
+    const int k0 = pin(kb * BK);
+    const int C = pin(a.C);
+    const int K = pin(a.K);
+    const int npq = pin(a.npq);
+    const int s_begin = pin((int)(((int64_t)split * a.slices) / a.splits));
+    const int s_end = pin((int)(((int64_t)(split + 1) * a.slices) / a.splits));
+    const int ns = s_end - s_begin;
+
+    const i32x4 x_desc = raw_descriptor(a.x, a.x_bytes);
+    const i32x4 dy_desc = raw_descriptor(a.dy, a.dy_bytes);
+
+    // Lane geometry of the loads. Block b = j*NW + wave of a slice covers
+    // 1024/ROW consecutive pixel rows; lane l fills row b*(1024/ROW) + l/CH at
+    // chunk position l % CH, which holds logical chunk (l % CH) ^ w_swizzle(row).
+    int x_row[X_INSTR], d_row[D_INSTR];
+    uint32_t x_c[X_INSTR];                // element offset of the lane's chunk within a row (c0 included)
+    uint32_t d_off[D_INSTR];              // byte offset of the lane's dy chunk within a pixel row (k0 included)
+    bool x_cok[X_INSTR], d_kok[D_INSTR];  // the chunk lies inside C / K
+#pragma unroll
+    for (int j = 0; j < X_INSTR; ++j) {
+        const int b = j * NW + wave;
+        x_row[j] = b * (1024 / XROW) + lane / XCH;
+        const int chunk = (lane % XCH) ^ w_swizzle<XROW>(x_row[j]);
+        x_c[j] = (uint32_t)(c0 + chunk * 8);
+        x_cok[j] = c0 + chunk * 8 < C;
+    }
+#pragma unroll
+    for (int j = 0; j < D_INSTR; ++j) {
+        const int b = j * NW + wave;
+        d_row[j] = b * (1024 / DROW) + lane / DCH;
+        const int chunk = (lane % DCH) ^ w_swizzle<DROW>(d_row[j]);
+        d_off[j] = (uint32_t)(k0 + chunk * 8) * 2u;
+        d_kok[j] = k0 + chunk * 8 < K;
+    }
+    const int Hh = a.H, Ww = a.W, str = a.stride, pad = a.pad;
+    // Issue the loads of slice si into LDS stage st.
+    auto issue = [&](int si, int st) {
+        const int m0 = si * BR;
+        const uint32_t base = lds_u32 + (uint32_t)(st * STAGE);
+#pragma unroll
+        for (int j = 0; j < X_INSTR; ++j) {
+            const int m = m0 + x_row[j];
+            const uint32_t n = fastdiv((uint32_t)m, a.div_pq);
+            const uint32_t rem = (uint32_t)m - n * a.div_pq.d;
+            const uint32_t p = fastdiv(rem, a.div_q);
+            const uint32_t q = rem - p * a.div_q.d;
+            const int h = (int)p * str - pad + r;
+            const int w = (int)q * str - pad + t;
+            const bool ok = x_cok[j] & (m < npq) & ((unsigned)h < (unsigned)Hh) & ((unsigned)w < (unsigned)Ww);
+            const uint32_t off = ((((n * (uint32_t)Hh + (uint32_t)h) * (uint32_t)Ww + (uint32_t)w) * (uint32_t)C) + x_c[j]) * 2u;
+            dma16(x_desc, ok ? off : 0x80000000u, 0u, base + (uint32_t)((j * NW + wave) * 1024));
+        }
+#pragma unroll
+        for (int j = 0; j < D_INSTR; ++j) {
+            const int m = m0 + d_row[j];
+            const bool ok = d_kok[j] & (m < npq);
+            dma16(dy_desc, ok ? (uint32_t)m * (uint32_t)K * 2u + d_off[j] : 0x80000000u, 0u,
+                  base + (uint32_t)(X_BYTES + (j * NW + wave) * 1024));
+        }
+    };
+
+    // Fragment addresses (bytes within a stage, sub-step 0): 32 columns of a
+    // [64 pixels][ROW] slice starting at column `col0`; group g = lane/16
+    // covers columns +16*(g&1), pixels +8*(g>>1); within it lane 4r+q reads
+    // pixel row r, columns 4q..4q+3 (two transpose reads give 8 pixels).
+    const int g = (lane >> 4) & 3;
+    const int rr = (lane & 15) >> 2;
+    const int qq = lane & 3;
+    const int prow = (g >> 1) * 8 + rr;
+    int xa[FN], db[FM];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int cl = wc * TC + fn * 32 + (g & 1) * 16 + 4 * qq;
+        xa[fn] = prow * XROW + (((cl >> 3) ^ w_swizzle<XROW>(prow)) * 16) + (cl & 7) * 2;
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int kl = wk * TK + fm * 32 + (g & 1) * 16 + 4 * qq;
+        db[fm] = X_BYTES + prow * DROW + (((kl >> 3) ^ w_swizzle<DROW>(prow)) * 16) + (kl & 7) * 2;
+    }
+    auto tr8 = [&](const lds_char* p, int row_bytes) -> half8_t {
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)p);
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p + 4 * row_bytes));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        return __builtin_bit_cast(half8_t, u32x4{l2.x, l2.y, h2.x, h2.y});
+    };
+
+    float16_t acc[FN][FM];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[fn][fm][e] = 0.0f;
+
+    auto compute = [&](int st) {
+        const lds_char* sb = (const lds_char*)lds + st * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < BR / 16; ++kk) {
+            half8_t af[FN], bf[FM];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                af[fn] = tr8(sb + xa[fn] + kk * 16 * XROW, XROW);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                bf[fm] = tr8(sb + db[fm] + kk * 16 * DROW, DROW);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[fn], bf[fm], acc[fn][fm], 0, 0, 0);
+        }
+    };
+
+    // The slice stream: requests run two slices ahead in a ring of three
+    // stages. Loads complete in issue order, so the wait for slice i allows
+    // exactly the LD loads of slice i+1 when those were issued.
+    if (ns > 0)
+        issue(s_begin, 0);
+    if (ns > 1)
+        issue(s_begin + 1, 1);
+    for (int i = 0; i < ns; ++i) {
+        if (i + 1 < ns)
+            wait_vmcnt<LD>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();        // every wave's part of slice i is in LDS, and every wave
+                                // is done with the stage the next request reuses
+        if (i + 2 < ns)
+            issue(s_begin + i + 2, (i + 2) % 3);
+        compute(i % 3);
+    }
+
+    // partial sums in register order: 16-byte group q of thread tid at float
+    // offset (q*NT + tid)*4 of this (split, tile) block
+    float* out = a.part + ((size_t)split * (size_t)tiles + (size_t)tile) * (size_t)(BC * BK);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int gi = (fn * FM + fm) * 4 + q;
+                *(float4_t*)(out + (size_t)(gi * NT + tid) * 4) =
+                    float4_t{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2], acc[fn][fm][4 * q + 3]};
+            }
+}
+
+// dw from the partial sums: one thread per 16-byte group of one tile; the
+// splits are added in order (so the result does not depend on timing), and
+// the group is mapped back to its 4 channels and output channel. In the
+// 32x32 accumulator block a lane holds rows 8*q + 4*(lane/32) .. +3 (here
+// channels) of column lane % 32 (here the output channel).
+template <int BC, int BK, int WC, int WK>
+__global__ void __launch_bounds__(256) wgrad_reduce(WgradArgs a)
+{
+    constexpr int NW = WC * WK;
+    constexpr int NT = 64 * NW;
+    constexpr int TC = BC / WC, TK = BK / WK;
+    constexpr int FM = TK / 32;
+    constexpr int GROUPS = BC * BK / 4;           // 16-byte groups per tile
+    const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+    if (u >= (uint32_t)a.tiles * (uint32_t)GROUPS)
+        return;
+    const int tile = (int)(u / GROUPS);
+    const int gq = (int)(u % GROUPS);
+    float4_t sum{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sp = 0; sp < a.splits; ++sp)
+        sum += *(const float4_t*)(a.part + (((size_t)sp * (size_t)a.tiles + (size_t)tile) * (size_t)GROUPS + (size_t)gq) * 4);
+    const int gi = gq / NT;
+    const int th = gq % NT;
+    const int wave = th / 64, lane = th % 64;
+    const int wc = wave % WC, wk = wave / WC;
+    const int fn = gi / (FM * 4), fm = (gi / 4) % FM, q = gi % 4;
+    const int kb = tile % a.tiles_k;
+    const int rest = tile / a.tiles_k;
+    const int cb = rest % a.tiles_c;
+    const int tap = rest / a.tiles_c;
+    const int c = cb * BC + wc * TC + fn * 32 + 8 * q + 4 * (lane >> 5);
+    const int k = kb * BK + wk * TK + fm * 32 + (lane & 31);
+    if (c < a.C && k < a.K)   // C is a multiple of 8: the 4 channels are all inside or all outside
+        *(float4_t*)(a.dw + ((size_t)k * (size_t)(a.R * a.S) + (size_t)tap) * (size_t)a.C + (size_t)c) = sum;
+}
+
+// The compiled wgrad tile configurations: (BC, BK, WC, WK).
+#define CBW_WGRAD_CONFIGS(X) \
+    X(128, 128, 2, 4)        \
+    X(256, 128, 4, 2)
+
+#define CBW_WGRAD_ENTRY(BC, BK, WC, WK) {BC, BK, WC, WK, #BC "x" #BK "/" #WC "x" #WK},
+const WgradConfig kWgradConfigs[] = {CBW_WGRAD_CONFIGS(CBW_WGRAD_ENTRY)};
+constexpr int kNumWgradConfigs = sizeof(kWgradConfigs) / sizeof(kWgradConfigs[0]);
+
+template <int BC, int BK, int WC, int WK>
+hipError_t wgrad_launch(const WgradArgs& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((wgrad_igemm<BC, BK, WC, WK>), dim3(a.tiles * a.splits), dim3(64 * WC * WK), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int BC, int BK, int WC, int WK>
+hipError_t wgrad_reduce_launch(const WgradArgs& a, hipStream_t stream)
+{
+    const uint32_t groups = (uint32_t)a.tiles * (uint32_t)(BC * BK / 4);
+    hipLaunchKernelGGL((wgrad_reduce<BC, BK, WC, WK>), dim3((groups + 255) / 256), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int BC, int BK, int WC, int WK>
+int wgrad_private(void)
+{
+    hipFuncAttributes a1, a2;
+    if (hipFuncGetAttributes(&a1, reinterpret_cast<const void*>(wgrad_igemm<BC, BK, WC, WK>)) != hipSuccess ||
+        hipFuncGetAttributes(&a2, reinterpret_cast<const void*>(wgrad_reduce<BC, BK, WC, WK>)) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return (int)(a1.localSizeBytes + a2.localSizeBytes);
+}
+
+using WgradLaunchFn = hipError_t (*)(const WgradArgs&, hipStream_t);
+#define CBW_WGRAD_LAUNCH(BC, BK, WC, WK) &wgrad_launch<BC, BK, WC, WK>,
+#define CBW_WGRAD_REDUCE(BC, BK, WC, WK) &wgrad_reduce_launch<BC, BK, WC, WK>,
+#define CBW_WGRAD_PRIVATE(BC, BK, WC, WK) &wgrad_private<BC, BK, WC, WK>,
+const WgradLaunchFn kWgradLaunch[] = {CBW_WGRAD_CONFIGS(CBW_WGRAD_LAUNCH)};
+const WgradLaunchFn kWgradReduce[] = {CBW_WGRAD_CONFIGS(CBW_WGRAD_REDUCE)};
+int (*const kWgradPrivate[])(void) = {CBW_WGRAD_CONFIGS(CBW_WGRAD_PRIVATE)};
+
+}  // namespace
+
+int wgrad_num_configs() { return kNumWgradConfigs; }
+
+const WgradConfig& wgrad_config(int id) { return kWgradConfigs[id]; }
+
+hipError_t launch_wgrad(int id, const WgradArgs& a, hipStream_t stream)
+{
+    if (id < 0 || id >= kNumWgradConfigs)
+        return hipErrorInvalidValue;
+    return kWgradLaunch[id](a, stream);
+}
+
+hipError_t launch_wgrad_reduce(int id, const WgradArgs& a, hipStream_t stream)
+{
+    if (id < 0 || id >= kNumWgradConfigs)
+        return hipErrorInvalidValue;
+    return kWgradReduce[id](a, stream);
+}
+
+int wgrad_private_bytes(int id)
+{
+    return (id >= 0 && id < kNumWgradConfigs) ? kWgradPrivate[id]() : -1;
+}
+
 }  // namespace cbw

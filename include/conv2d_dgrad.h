@@ -194,6 +194,47 @@ int conv2d_dgrad_check(const void* dy, const void* w, void* dx,
                        int N, int H, int W, int C, int K, int R, int S,
                        int stride, int pad, int epilogue, const void* z);
 
+/*
+ * Filter gradient (wgrad) of the same forward layer:
+ *
+ *   dw[k,r,t,c] = sum over n,p,q of dy[n,p,q,k] * x[n, p*s - pad + r, q*s - pad + t, c],
+ *
+ * where input positions in the padding contribute zero. This is the other
+ * half of conv backward, which the "[CUTLASS] Conv2d dgrad" page (apache/tvm
+ * PR #10110) leaves for later because of its accuracy issues.
+ *
+ * Arguments:
+ *   dy [N][P][Q][K]   fp16, as for conv2d_dgrad_nhwc
+ *   x  [N][H][W][C]   fp16 NHWC input of the forward layer
+ *   dw [K][R][S][C]   fp32, fully written (never read)
+ * Shapes, alignment (16 bytes), limits and status codes are those of
+ * conv2d_dgrad_nhwc; dw must not overlap dy or x.
+ *
+ * Accumulation is fp32 throughout: the N*P*Q-long reduction is cut into
+ * contiguous ranges whose fp32 partial sums a second kernel adds in a fixed
+ * order, so results do not depend on timing. The partial sums live in a
+ * library-owned device workspace per device and stream (at most 1 GiB),
+ * allocated on first use outside graph capture and never freed. Calls are
+ * asynchronous on `stream`.
+ */
+int conv2d_wgrad_nhwc(const void* dy, const void* x, void* dw,
+                      int N, int H, int W, int C, int K, int R, int S,
+                      int stride, int pad, void* stream);
+
+/* The same with an explicit tile configuration (0 .. conv2d_wgrad_num_configs()-1)
+ * and reduction split count (0: automatic, about two workgroups per CU). */
+int conv2d_wgrad_nhwc_config(const void* dy, const void* x, void* dw,
+                             int N, int H, int W, int C, int K, int R, int S,
+                             int stride, int pad, int config_id, int splits, void* stream);
+
+/* Number of compiled wgrad tile configurations. */
+int conv2d_wgrad_num_configs(void);
+
+/* Validation alone (no HIP call) for conv2d_wgrad_nhwc. */
+int conv2d_wgrad_check(const void* dy, const void* x, void* dw,
+                       int N, int H, int W, int C, int K, int R, int S,
+                       int stride, int pad);
+
 /* Thread-local text of the last error ("" if none). */
 const char* conv2d_dgrad_last_error(void);
 

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "conv2d_dgrad.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(conv2d_dgrad_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(conv2d_[dw]grad_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -84,6 +84,41 @@ def test_validation_codes(kw, code):
     assert check(**kw) == code
     if code != cb.OK:
         assert cb.conv2d_dgrad_last_error() != ""
+
+
+WG = dict(N=2, H=8, W=8, C=16, K=8, R=3, S=3, stride=2, pad=1)
+
+
+def wcheck(dy=DY, x=DX, dw=WP, **kw):
+    args = dict(WG)
+    args.update(kw)
+    return cb.conv2d_wgrad_check(dy, x, dw, args["N"], args["H"], args["W"], args["C"], args["K"],
+                                 args["R"], args["S"], args["stride"], args["pad"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, cb.OK),
+    ({"N": 0}, cb.INVALID_ARGUMENT), ({"stride": 0}, cb.INVALID_ARGUMENT), ({"H": 1, "R": 5, "pad": 0}, cb.INVALID_ARGUMENT),
+    ({"dy": 0}, cb.INVALID_ARGUMENT), ({"x": 0}, cb.INVALID_ARGUMENT), ({"dw": 0}, cb.INVALID_ARGUMENT),
+    ({"dw": WP + 8}, cb.INVALID_ARGUMENT),                          # misaligned
+    ({"dw": DY + 64}, cb.INVALID_ARGUMENT),                         # dw overlaps dy
+    ({"dw": DX + 16}, cb.INVALID_ARGUMENT),                         # dw overlaps x
+    ({"C": 12}, cb.UNSUPPORTED), ({"K": 4}, cb.UNSUPPORTED),
+])
+def test_wgrad_validation_codes(kw, code):
+    assert wcheck(**kw) == code
+    if code != cb.OK:
+        assert cb.conv2d_dgrad_last_error() != ""
+
+
+def test_wgrad_configs_and_bad_calls():
+    assert cb.conv2d_wgrad_num_configs() >= 2
+    with pytest.raises(cb.DgradError) as e:
+        cb.conv2d_wgrad_nhwc(DY, DX, WP, 2, 8, 8, 12, 8, 3, 3, 1, 1, stream=0)
+    assert e.value.code == cb.UNSUPPORTED
+    with pytest.raises(cb.DgradError) as e:
+        cb.conv2d_wgrad_nhwc_config(DY, DX, WP, 2, 8, 8, 16, 8, 3, 3, 1, 1, config_id=99, stream=0)
+    assert e.value.code == cb.INVALID_ARGUMENT
 
 
 def test_invalid_call_returns_before_any_hip_call():

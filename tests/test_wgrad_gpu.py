@@ -1,0 +1,120 @@
+"""GPU parity of wgrad (the filter gradient) through the C ABI against the
+fp64 oracle.
+
+Tolerance. Every fp16 x fp16 product is exact in fp32. The kernel adds them
+in fp32: 16 at a time inside an MFMA, then along its slice range (at most a
+few hundred sequential adds of partial sums per output), then the split
+partials in order. Each add rounds by at most 2^-24 of a partial sum, which
+is bounded by sum|dy * x|, so |gpu - ref| <= ~400 * 2^-24 * sum|dy * x|;
+the test allows 1e-4 * sum|dy * x| + 1e-6 (4x that). Integer inputs make
+every partial sum an exact fp32 integer: there the result is bit-exact.
+"""
+import numpy as np
+import pytest
+
+import convolution_backward_amd as cb
+import oracle
+from workloads import CONFIGS, integer_inputs, make_inputs, small_config
+from tests.gpu_util import note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    (2, 15, 13, 136, 72, 3, 3, 1, 1),
+    (2, 17, 16, 64, 128, 3, 3, 2, 1),
+    (3, 11, 12, 40, 24, 3, 3, 2, 0),
+    (1, 20, 19, 32, 16, 1, 1, 2, 0),
+    (2, 9, 9, 16, 16, 5, 5, 3, 2),
+    (1, 14, 14, 264, 56, 1, 1, 1, 0),
+    (2, 8, 10, 24, 8, 2, 4, 2, 1),
+    (1, 1, 1, 8, 8, 1, 1, 1, 0),
+    (1, 5, 5, 8, 8, 7, 7, 1, 3),
+    (4, 28, 28, 192, 320, 3, 3, 1, 1),
+]
+
+
+def _x_like(cfg, seed, integer=False):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (cfg.N, cfg.H, cfg.W, cfg.C)
+    if integer:
+        return rng.integers(-2, 3, size=shape).astype(np.float16)
+    return rng.standard_normal(shape).astype(np.float16)
+
+
+def run_wgrad(cfg, dy, x, config_id=None, splits=0, stream=None):
+    import torch
+    d_dy, d_x = to_dev(dy), to_dev(x)
+    dw = torch.full((cfg.K, cfg.R, cfg.S, cfg.C), float("nan"), dtype=torch.float32, device="cuda")
+    if stream is None:
+        cb.wgrad(d_dy, d_x, cfg.R, cfg.S, cfg.stride, cfg.pad, config_id=config_id, splits=splits, out=dw)
+    else:
+        with torch.cuda.stream(stream):
+            cb.wgrad(d_dy, d_x, cfg.R, cfg.S, cfg.stride, cfg.pad, config_id=config_id, splits=splits, out=dw)
+        stream.synchronize()
+    torch.cuda.synchronize()
+    return dw.cpu().numpy()
+
+
+def assert_wgrad_close(got, ref, mag, what):
+    g = np.asarray(got, dtype=np.float64)
+    assert not np.isnan(g).any(), f"{what}: NaN (unwritten element?)"
+    err = np.abs(g - ref)
+    bound = 1e-4 * mag + 1e-6
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} out of tolerance; max err {err.max():.3g}, "
+                           f"worst ratio {np.max(err / bound):.3g}")
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_wgrad_small_every_config(shape):
+    cfg = small_config(*shape)
+    dy = make_inputs(cfg)["dy"]
+    x = _x_like(cfg, 41)
+    ref, mag = oracle.wgrad(dy, x, cfg.R, cfg.S, cfg.stride, cfg.pad, with_abs=True)
+    for cid in range(cb.conv2d_wgrad_num_configs()):
+        for splits in (0, 1, 3):
+            note(f"wgrad small {shape} config {cid} splits {splits}")
+            assert_wgrad_close(run_wgrad(cfg, dy, x, cid, splits), ref, mag, f"{shape} config {cid} splits {splits}")
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_wgrad_integer_bit_exact(shape):
+    cfg = small_config(*shape)
+    dy = integer_inputs(cfg, lo=-2, hi=2, seed=42)["dy"]
+    x = _x_like(cfg, 43, integer=True)
+    ref = oracle.wgrad(dy, x, cfg.R, cfg.S, cfg.stride, cfg.pad)
+    for cid in range(cb.conv2d_wgrad_num_configs()):
+        note(f"wgrad integer {shape} config {cid}")
+        got = run_wgrad(cfg, dy, x, cid, 0)
+        assert not np.isnan(got).any()
+        assert np.array_equal(got.astype(np.float64), ref), f"{np.sum(got != ref)} elements differ"
+
+
+@pytest.mark.parametrize("idx", range(1, len(CONFIGS)), ids=[c.name for c in CONFIGS[1:]])
+def test_wgrad_measured_layer(idx):
+    """Each measured layer's shape at full size (automatic config and split):
+    sampled filter rows against the oracle, the whole tensor checked for
+    unwritten elements, and the same bits on a second call."""
+    cfg = CONFIGS[idx]
+    dy = make_inputs(cfg)["dy"]
+    x = _x_like(cfg, 44)
+    note(f"wgrad measured layer {cfg.name}")
+    got = run_wgrad(cfg, dy, x)
+    assert not np.isnan(got).any()
+    rng = np.random.Generator(np.random.PCG64(45 + idx))
+    nrow = cfg.K * cfg.R * cfg.S
+    rows = np.unique(np.concatenate([rng.choice(nrow, size=min(6, nrow), replace=False), [0, nrow - 1]]))
+    ref, mag = oracle.wgrad(dy, x, cfg.R, cfg.S, cfg.stride, cfg.pad, rows=rows, with_abs=True)
+    assert_wgrad_close(got.reshape(-1, cfg.C)[rows], ref, mag, cfg.name)
+    again = run_wgrad(cfg, dy, x)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32)), "wgrad changed between calls"
+
+
+def test_wgrad_side_stream():
+    import torch
+    cfg = small_config(2, 15, 13, 136, 72, 3, 3, 2, 1)
+    dy = make_inputs(cfg)["dy"]
+    x = _x_like(cfg, 46)
+    ref, mag = oracle.wgrad(dy, x, cfg.R, cfg.S, cfg.stride, cfg.pad, with_abs=True)
+    note("wgrad side stream")
+    assert_wgrad_close(run_wgrad(cfg, dy, x, stream=torch.cuda.Stream()), ref, mag, "side stream")

@@ -144,6 +144,15 @@ def make_inputs(cfg, seed=None) -> dict:
     return out
 
 
+def make_x(cfg, seed=None) -> np.ndarray:
+    """The forward layer's input x [N,H,W,C] for wgrad: post-ReLU activations,
+    max(N(0,1), 0) rounded to float16 (half of the values are exact zeros)."""
+    cfg = get_config(cfg)
+    rng = np.random.Generator(np.random.PCG64((cfg.seed + 500) if seed is None else seed))
+    x = rng.standard_normal(size=(cfg.N, cfg.H, cfg.W, cfg.C), dtype=np.float64)
+    return np.maximum(x, 0.0).astype(np.float16)
+
+
 def small_config(N, H, W, C, K, R, S, stride, pad, epilogue=EPI_NONE,
                  seed=7, w_std=None, name="small") -> DgradConfig:
     """An arbitrary shape with the batch-256 value recipe (dy ~ N(0,1),
