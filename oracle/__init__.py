@@ -59,6 +59,10 @@ def _bind(lib):
     lib.oracle_dgrad_full.restype = i
     lib.oracle_wgrad_rows.argtypes = [u16p, u16p] + [i] * 9 + [i64p, ctypes.c_int64, f64p, f64p, i]
     lib.oracle_wgrad_rows.restype = i
+    lib.oracle_forward_rows.argtypes = [u16p, u16p, u16p] + [i] * 10 + [i64p, ctypes.c_int64, f64p, f64p, i]
+    lib.oracle_forward_rows.restype = i
+    lib.oracle_hardswish.argtypes = [ctypes.c_double]
+    lib.oracle_hardswish.restype = ctypes.c_double
     lib.oracle_round_to_half.argtypes = [f64p, u16p, ctypes.c_int64]
     lib.oracle_round_to_half.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -159,6 +163,41 @@ def wgrad(dy, x, R, S, stride, pad, rows=None, with_abs=False, threads=0, lib=No
         out = out.reshape(K, R, S, C)
         mag = mag.reshape(K, R, S, C) if with_abs else None
     return (out, mag) if with_abs else out
+
+
+def forward(x, w, bias, stride, pad, act=1, rows=None, threads=0, lib=None):
+    """fp64 forward layer of float16 x [N,H,W,C], w [K,R,S,C], bias [K]:
+    z = bias + conv(x, w) and y = hardswish(z) (act=1) or z (act=0).
+
+    Returns (z, y) of shape [N,P,Q,K], or [len(rows), K] when ``rows`` (linear
+    output pixels (n*P + p)*Q + q) is given.
+    """
+    lib = lib or load()
+    N, H, W, C = x.shape
+    K, R, S, C2 = w.shape
+    if C2 != C or tuple(bias.shape) != (K,):
+        raise ValueError("x, w and bias disagree on C or K")
+    P, Q = lib.oracle_out_extent(H, R, stride, pad), lib.oracle_out_extent(W, S, stride, pad)
+    xk, xp = _u16(x)
+    wk, wp = _u16(w)
+    bk, bp = _u16(bias)
+    rr = np.arange(N * P * Q, dtype=np.int64) if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    z = np.empty((len(rr), K), dtype=np.float64)
+    y = np.empty((len(rr), K), dtype=np.float64)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    rc = lib.oracle_forward_rows(xp, wp, bp, N, H, W, C, K, R, S, stride, pad, act,
+                                 rr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(rr),
+                                 z.ctypes.data_as(f64p), y.ctypes.data_as(f64p), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_forward failed with code {rc}")
+    del xk, wk, bk
+    if rows is None:
+        return z.reshape(N, P, Q, K), y.reshape(N, P, Q, K)
+    return z, y
+
+
+def hardswish(zv: float, lib=None) -> float:
+    return (lib or load()).oracle_hardswish(zv)
 
 
 def round_to_half(x, lib=None) -> np.ndarray:

@@ -37,7 +37,8 @@
  * Layouts: dy [N][P][Q][K], w [K][R][S][C], z and dx [N][H][W][C], all
  * C-contiguous. Output rows are linear pixel indices (n*H + h)*W + w.
  *
- * The file also holds the filter gradient (wgrad) of the same layer, below.
+ * The file also holds the filter gradient (wgrad) of the same layer and the
+ * forward layer with its bias + hardswish epilogue, below.
  */
 #include <math.h>
 #include <stdint.h>
@@ -354,6 +355,103 @@ int oracle_wgrad_rows(const uint16_t* dy, const uint16_t* x,
                 out[it * (int64_t)C + c] = sum[c];
                 if (abs_out)
                     abs_out[it * (int64_t)C + c] = mag[c];
+            }
+        }
+        free(acc);
+    }
+    free(lut);
+    return failed ? 2 : 0;
+}
+
+/* ---- forward conv + bias + hardswish, one output pixel at a time --------- */
+
+/* hardswish(z) = z * min(max(z + 3, 0), 6) / 6, the activation of the Bolt
+ * paper notes' Conv2D + BiasAdd + Hardswish fusion. */
+double oracle_hardswish(double z)
+{
+    double g = z + 3.0;
+    if (g < 0.0)
+        g = 0.0;
+    if (g > 6.0)
+        g = 6.0;
+    return z * g / 6.0;
+}
+
+/*
+ * The forward layer itself with the fused bias + activation epilogue that
+ * the Bolt notes describe (Conv2D + BiasAdd + Hardswish):
+ *   z[n,p,q,k] = bias[k] + sum over r,t,c of x[n, p*s - pad + r, q*s - pad + t, c] * w[k,r,t,c]
+ *   y = hardswish(z) (act = 1) or y = z (act = 0),
+ * where input positions in the padding contribute zero.
+ *
+ * rows: linear output pixel indices (n*P + p)*Q + q; z_out, y_out: [nrows][K]
+ * (either may be NULL). Returns 0 on success, 1 on invalid arguments, 2 on
+ * allocation failure.
+ */
+int oracle_forward_rows(const uint16_t* x, const uint16_t* wt, const uint16_t* bias,
+                        int N, int H, int W, int C, int K, int R, int S,
+                        int stride, int pad, int act,
+                        const int64_t* rows, int64_t nrows, double* z_out, double* y_out, int nthreads)
+{
+    if (check_args(N, H, W, C, K, R, S, stride, pad, ORACLE_EPI_NONE, NULL) || act < 0 || act > 1)
+        return 1;
+    if (nrows < 0 || (nrows > 0 && rows == NULL) || x == NULL || wt == NULL || bias == NULL)
+        return 1;
+    const int P = oracle_out_extent(H, R, stride, pad);
+    const int Q = oracle_out_extent(W, S, stride, pad);
+    const int64_t nout = (int64_t)N * P * Q;
+    for (int64_t i = 0; i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= nout)
+            return 1;
+    double* lut = (double*)malloc(sizeof(double) * 65536);
+    if (!lut)
+        return 2;
+    for (int b = 0; b < 65536; ++b)
+        lut[b] = oracle_half_to_double((uint16_t)b);
+    if (nthreads < 1)
+        nthreads = omp_get_max_threads();
+    int failed = 0;
+
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* acc = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t it = 0; it < nrows; ++it) {
+            if (!acc)
+                continue;
+            const int64_t pix = rows[it];
+            const int n = (int)(pix / ((int64_t)P * Q));
+            const int p = (int)((pix / Q) % P);
+            const int q = (int)(pix % Q);
+            for (int k = 0; k < K; ++k)
+                acc[k] = lut[bias[k]];
+            for (int r = 0; r < R; ++r) {
+                const int h = p * stride - pad + r;
+                if (h < 0 || h >= H)
+                    continue;
+                for (int t = 0; t < S; ++t) {
+                    const int w = q * stride - pad + t;
+                    if (w < 0 || w >= W)
+                        continue;
+                    const uint16_t* xrow = x + (((int64_t)n * H + h) * W + w) * C;
+                    for (int k = 0; k < K; ++k) {
+                        const uint16_t* wrow = wt + (((int64_t)k * R + r) * S + t) * C;
+                        double sum = 0.0;
+                        for (int c = 0; c < C; ++c)
+                            sum += lut[xrow[c]] * lut[wrow[c]];
+                        acc[k] += sum;
+                    }
+                }
+            }
+            for (int k = 0; k < K; ++k) {
+                if (z_out)
+                    z_out[it * (int64_t)K + k] = acc[k];
+                if (y_out)
+                    y_out[it * (int64_t)K + k] = act ? oracle_hardswish(acc[k]) : acc[k];
             }
         }
         free(acc);

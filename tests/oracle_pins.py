@@ -470,6 +470,78 @@ def check_wgrad_rows_and_abs(lib):
     assert np.all(mag >= np.abs(full) - 1e-12)
 
 
+# ----------------------------------------------------------------- forward pins
+
+
+def check_forward_hand_examples(lib):
+    """x = W9 (one channel), 3x3 filter of ones, one output channel.
+
+    No padding: z = bias + 45 (the sum of 1..9). With bias -40, z = 5 and
+    hardswish(5) = 5 * min(8, 6) / 6 = 5; with bias -44, z = 1 and
+    hardswish(1) = 1 * 4 / 6 = 2/3; with bias -50, z = -5 and hardswish = 0.
+    Padding 1, bias 0: the 3x3 output is the window sums
+    [[12, 21, 16], [27, 45, 33], [24, 39, 28]] (rows 0-1 / all / 1-2 and
+    columns alike), and act = 0 returns z itself.
+    """
+    x = f16(W9.reshape(1, 3, 3, 1))
+    w = f16(np.ones((1, 3, 3, 1)))
+    for b, zz, yy in [(-40.0, 5.0, 5.0), (-44.0, 1.0, 2.0 / 3.0), (-50.0, -5.0, 0.0)]:
+        z, y = oracle.forward(x, w, f16([b]), 1, 0, act=1, lib=lib)
+        assert z.reshape(()) == zz and np.isclose(y.reshape(()), yy, rtol=0, atol=1e-15)
+    z, y = oracle.forward(x, w, f16([0.0]), 1, 1, act=0, lib=lib)
+    want = np.array([[12, 21, 16], [27, 45, 33], [24, 39, 28]], float)
+    assert np.array_equal(z.reshape(3, 3), want) and np.array_equal(y.reshape(3, 3), want)
+
+
+FWD_CASES = [(2, 7, 6, 3, 4, 3, 3, 2, 1), (1, 8, 8, 2, 3, 3, 3, 1, 1), (2, 6, 7, 4, 2, 1, 1, 2, 0),
+             (1, 9, 8, 3, 2, 5, 3, 3, 2), (1, 5, 5, 2, 2, 2, 4, 1, 0)]
+
+
+def _fwd_inputs(rng, N, H, W, C, K, R, S):
+    return (f16(rng.standard_normal((N, H, W, C))), f16(rng.standard_normal((K, R, S, C))),
+            f16(rng.standard_normal(K)))
+
+
+def check_forward_vs_slicing(lib):
+    """z equals the slicing forward plus bias, and y the textbook hardswish of z."""
+    rng = np.random.Generator(np.random.PCG64(40))
+    for (N, H, W, C, K, R, S, s, pad) in FWD_CASES:
+        x, w, b = _fwd_inputs(rng, N, H, W, C, K, R, S)
+        z, y = oracle.forward(x, w, b, s, pad, act=1, lib=lib)
+        ref = forward_conv(x, w, s, pad) + b.astype(np.float64)
+        assert np.allclose(z, ref, rtol=1e-12, atol=1e-12)
+        assert np.allclose(y, np.vectorize(hardswish)(z), rtol=1e-15, atol=1e-15)
+
+
+def check_forward_torch(lib):
+    """Cross-check with PyTorch's CPU fp64 conv2d (NCHW) and hardswish."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(41))
+    for (N, H, W, C, K, R, S, s, pad) in FWD_CASES:
+        x, w, b = _fwd_inputs(rng, N, H, W, C, K, R, S)
+        zt = torch.nn.functional.conv2d(
+            torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2),
+            torch.from_numpy(w.astype(np.float64)).permute(0, 3, 1, 2),
+            torch.from_numpy(b.astype(np.float64)), stride=s, padding=pad)
+        yt = torch.nn.functional.hardswish(zt)
+        z, y = oracle.forward(x, w, b, s, pad, act=1, lib=lib)
+        assert np.allclose(z, zt.permute(0, 2, 3, 1).numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(y, yt.permute(0, 2, 3, 1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def check_forward_adjoint_dgrad(lib):
+    """<z - bias, dy> = <x, dgrad(dy, w)>: the forward's adjoint is the
+    (separately pinned) dgrad."""
+    rng = np.random.Generator(np.random.PCG64(42))
+    for (N, H, W, C, K, R, S, s, pad) in FWD_CASES:
+        x, w, b = _fwd_inputs(rng, N, H, W, C, K, R, S)
+        z, _ = oracle.forward(x, w, b, s, pad, act=0, lib=lib)
+        dy = f16(rng.standard_normal(z.shape))
+        lhs = np.sum((z - b.astype(np.float64)) * dy.astype(np.float64))
+        rhs = np.sum(x.astype(np.float64) * oracle.dgrad(dy, w, H, W, s, pad, lib=lib))
+        assert np.isclose(lhs, rhs, rtol=1e-11, atol=1e-11)
+
+
 ALL_CHECKS = [
     check_fp16_decode, check_fp16_rne_encode, check_out_extent, check_hand_examples,
     check_scatter_bruteforce, check_adjoint_identity, check_adjoint_unit_vectors,
@@ -478,6 +550,7 @@ ALL_CHECKS = [
     check_wgrad_hand_examples, check_wgrad_adjoint_forward, check_wgrad_adjoint_dgrad,
     check_wgrad_unit_vectors, check_wgrad_matmul_special_cases, check_wgrad_torch_conv2d_weight,
     check_wgrad_rows_and_abs,
+    check_forward_hand_examples, check_forward_vs_slicing, check_forward_torch, check_forward_adjoint_dgrad,
 ]
 
 

@@ -40,6 +40,10 @@ MUTANTS = {
     "wgrad_input_transposed": ("x + (((int64_t)n * H + h) * W + w) * C", "x + (((int64_t)n * W + w) * H + h) * C"),
     "wgrad_signed_magnitude": ("mag[c] += fabs(v);", "mag[c] += v;"),
     "wgrad_stride_ignored": ("const int w = q * stride - pad + t;", "const int w = q - pad + t;"),
+    "forward_bias_dropped": ("acc[k] = lut[bias[k]];", "acc[k] = 0.0;"),
+    "forward_hardswish_clamp": ("if (g > 6.0)", "if (g > 3.0)"),
+    "forward_filter_taps_swapped": ("wt + (((int64_t)k * R + r) * S + t) * C", "wt + (((int64_t)k * S + t) * R + r) * C"),
+    "forward_output_decode": ("const int p = (int)((pix / Q) % P);", "const int p = (int)((pix / P) % Q);"),
 }
 
 _CHILD = r"""
