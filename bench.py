@@ -111,6 +111,8 @@ def main():
                     help="cold-cache launches per layer, each after a 512 MiB scratch write (0 skips)")
     ap.add_argument("--wgrad-reps", type=int, default=10,
                     help="timed wgrad (filter gradient) calls per layer, after the dgrad timing (0 skips)")
+    ap.add_argument("--forward-reps", type=int, default=10,
+                    help="timed forward (conv + bias + hardswish) calls per layer shape, after the rest (0 skips)")
     ap.add_argument("--only", default="",
                     help="comma-separated layer names: time only these (for profiler runs)")
     ap.add_argument("--copy-calibrate-mb", type=float, default=0.0,
@@ -279,6 +281,51 @@ def main():
                  "value": sum(cfg.useful_flops() for cfg, _ in layers) / wsum / 1e12, "unit": "TFLOP/s",
                  "layers": wlayers}
 
+    # ---- forward layer with the fused bias + hardswish epilogue (a NEXT row):
+    # each layer shape's x and w, seeded bias, z and y both stored; not part of `value`
+    fwd = None
+    if args.forward_reps > 0:
+        flayers = []
+        for cfg, d in layers:
+            x = torch.from_numpy(make_x(cfg)).to(dev)
+            bias = torch.from_numpy((np.random.Generator(np.random.PCG64(cfg.seed + 700))
+                                     .standard_normal(cfg.K) * 0.5).astype(np.float16)).to(dev)
+            y = torch.empty((cfg.N, cfg.P, cfg.Q, cfg.K), dtype=torch.float16, device=dev)
+            z = torch.empty_like(y)
+
+            def fcall():
+                cb.conv2d_forward_nhwc(x, d["w"], bias, z, y, cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
+                                       cfg.stride, cfg.pad, cb.ACT_HARDSWISH, stream.cuda_stream)
+            for _ in range(3):
+                fcall()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.forward_reps)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                fcall()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+            avg = float(np.mean(ms))
+            fl = cfg.useful_flops()
+            nbytes = 2 * (cfg.N * cfg.H * cfg.W * cfg.C + cfg.K * cfg.R * cfg.S * cfg.C + cfg.K
+                          + 2 * cfg.N * cfg.P * cfg.Q * cfg.K)
+            if fl / nbytes >= RIDGE:
+                rl = {"bound": "mfma", "achieved": fl / (avg * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
+            else:
+                rl = {"bound": "hbm", "achieved": nbytes / (avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+            rl["frac"] = rl["achieved"] / rl["peak"]
+            flayers.append({"layer": cfg.name, "avg_us": avg * 1e3, "min_us": float(np.min(ms)) * 1e3,
+                            "tflops": fl / (avg * 1e-3) / 1e12, "alg_mb": nbytes / 1e6, "roofline": rl})
+            log(f"[fwd] {cfg.name:34s} {avg*1e3:9.2f} us  {flayers[-1]['tflops']:7.1f} TFLOP/s  "
+                f"{rl['bound']} {rl['frac']:.1%}")
+            del x, bias, y, z
+        fsum = sum(f["avg_us"] for f in flayers) * 1e-6
+        fwd = {"note": "z = bias + conv(x, w), y = hardswish(z), both fp16 and stored; x = max(N(0,1),0), bias "
+                       "N(0,0.25) seeded; suite value = useful FLOPs / sum of per-layer means",
+               "value": sum(cfg.useful_flops() for cfg, _ in layers) / fsum / 1e12, "unit": "TFLOP/s",
+               "layers": flayers}
+
     flops = sum(cfg.useful_flops() for cfg, _ in layers)
     kernel_ms = sum(p["avg_us"] for p in per_layer) / 1e3
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -321,6 +368,7 @@ def main():
         "layers": per_layer,
         "cold": cold,
         "wgrad": wgrad,
+        "forward": fwd,
         "device": torch.cuda.get_device_name(dev),
         "build": cb.conv2d_dgrad_build_info(),
     }

@@ -62,6 +62,10 @@ def _bind(lib):
     lib.conv2d_wgrad_nhwc_config.argtypes = [vp, vp, vp] + [i] * 9 + [i, i, vp]
     lib.conv2d_wgrad_num_configs.argtypes = []
     lib.conv2d_wgrad_check.argtypes = [vp, vp, vp] + [i] * 9
+    lib.conv2d_forward_nhwc.argtypes = [vp] * 5 + [i] * 10 + [vp]
+    lib.conv2d_forward_nhwc_config.argtypes = [vp] * 5 + [i] * 10 + [i, vp]
+    lib.conv2d_forward_num_configs.argtypes = []
+    lib.conv2d_forward_check.argtypes = [vp] * 5 + [i] * 10
     lib.conv2d_dgrad_last_error.argtypes = []
     lib.conv2d_dgrad_last_error.restype = ctypes.c_char_p
     lib.conv2d_dgrad_build_info.argtypes = []
@@ -70,7 +74,9 @@ def _bind(lib):
                  "conv2d_dgrad_config_name", "conv2d_dgrad_query_config", "conv2d_dgrad_set_autotune",
                  "conv2d_dgrad_set_streamk", "conv2d_dgrad_streamk_launches", "conv2d_dgrad_cache_clear", "conv2d_dgrad_cache_size", "conv2d_dgrad_cache_save",
                  "conv2d_dgrad_cache_load", "conv2d_dgrad_plan", "conv2d_dgrad_check",
-                 "conv2d_wgrad_nhwc", "conv2d_wgrad_nhwc_config", "conv2d_wgrad_num_configs", "conv2d_wgrad_check"):
+                 "conv2d_wgrad_nhwc", "conv2d_wgrad_nhwc_config", "conv2d_wgrad_num_configs", "conv2d_wgrad_check",
+                 "conv2d_forward_nhwc", "conv2d_forward_nhwc_config", "conv2d_forward_num_configs",
+                 "conv2d_forward_check"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -181,6 +187,57 @@ def wgrad(dy, x, R, S, stride, pad, config_id=None, splits=0, out=None):
     return dw
 
 
+ACT_NONE, ACT_HARDSWISH = 0, 1
+
+
+def conv2d_forward_nhwc(x, w, bias, z, y, N, H, W, C, K, R, S, stride, pad, act=ACT_HARDSWISH, stream=None):
+    """z = bias + conv(x, w) (if z is given) and y = act(z), enqueued on `stream`."""
+    return _check(get_lib().conv2d_forward_nhwc(_ptr(x), _ptr(w), _ptr(bias), _ptr(z), _ptr(y), N, H, W, C, K, R,
+                                                S, stride, pad, act, _stream(stream, x, y)))
+
+
+def conv2d_forward_nhwc_config(x, w, bias, z, y, N, H, W, C, K, R, S, stride, pad, act=ACT_HARDSWISH,
+                               config_id=0, stream=None):
+    return _check(get_lib().conv2d_forward_nhwc_config(_ptr(x), _ptr(w), _ptr(bias), _ptr(z), _ptr(y), N, H, W, C,
+                                                       K, R, S, stride, pad, act, config_id, _stream(stream, x, y)))
+
+
+def conv2d_forward_check(x, w, bias, z, y, N, H, W, C, K, R, S, stride, pad, act=ACT_HARDSWISH) -> int:
+    """Validation only: the status code, no exception, no HIP call."""
+    return get_lib().conv2d_forward_check(_ptr(x), _ptr(w), _ptr(bias), _ptr(z), _ptr(y), N, H, W, C, K, R, S,
+                                          stride, pad, act)
+
+
+def conv2d_forward_num_configs() -> int:
+    return get_lib().conv2d_forward_num_configs()
+
+
+def forward(x, w, bias, stride, pad, act=ACT_HARDSWISH, with_z=True, config_id=None, out=None, z_out=None):
+    """Allocate y (and z) [N,P,Q,K] float16 with torch.empty and fill them on the
+    current stream. Returns (z, y) (z is None when with_z is False).
+
+    x [N,H,W,C], w [K,R,S,C] and bias [K] are float16 GPU tensors.
+    """
+    import torch
+    for name, t in (("x", x), ("w", w), ("bias", bias)):
+        if t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
+    N, H, W, C = x.shape
+    K, R, S, C2 = w.shape
+    if C2 != C:
+        raise ValueError("x and w disagree on C")
+    P, Q = (H + 2 * pad - R) // stride + 1, (W + 2 * pad - S) // stride + 1
+    y = out if out is not None else torch.empty((N, P, Q, K), dtype=torch.float16, device=x.device)
+    z = None
+    if with_z:
+        z = z_out if z_out is not None else torch.empty((N, P, Q, K), dtype=torch.float16, device=x.device)
+    if config_id is None:
+        conv2d_forward_nhwc(x, w, bias, z, y, N, H, W, C, K, R, S, stride, pad, act)
+    else:
+        conv2d_forward_nhwc_config(x, w, bias, z, y, N, H, W, C, K, R, S, stride, pad, act, config_id)
+    return z, y
+
+
 def conv2d_dgrad_num_configs() -> int:
     return get_lib().conv2d_dgrad_num_configs()
 
@@ -282,5 +339,7 @@ __all__ = [
     "conv2d_dgrad_cache_clear", "conv2d_dgrad_cache_size", "conv2d_dgrad_cache_save", "conv2d_dgrad_cache_load",
     "conv2d_dgrad_plan", "conv2d_dgrad_last_error", "conv2d_dgrad_build_info", "dgrad", "get_lib",
     "conv2d_wgrad_nhwc", "conv2d_wgrad_nhwc_config", "conv2d_wgrad_check", "conv2d_wgrad_num_configs", "wgrad",
+    "conv2d_forward_nhwc", "conv2d_forward_nhwc_config", "conv2d_forward_check", "conv2d_forward_num_configs",
+    "forward", "ACT_NONE", "ACT_HARDSWISH",
     "DgradError", "EPI_NONE", "EPI_DRELU", "EPI_DHARDSWISH",
 ]

@@ -148,6 +148,39 @@ hipError_t launch_wgrad(int id, const WgradArgs& a, hipStream_t stream);
 hipError_t launch_wgrad_reduce(int id, const WgradArgs& a, hipStream_t stream);
 int wgrad_private_bytes(int id);   // scratch bytes per lane of both kernels, -1 if unknown
 
+// ------------------------------------------------------------------ forward
+
+// The forward layer with its fused epilogue (see fwd_igemm in
+// dgrad_kernels.hip): z[m,k] = bias[k] + sum over taps and c of
+// x[n, p*s-pad+r, q*s-pad+t, c] * w[k,r,t,c] for output pixel m = (n,p,q),
+// y = hardswish(z) (act 1) or z (act 0). GEMM rows are output pixels, columns
+// output channels, the reduction runs tap by tap over C in 64-wide slices.
+struct FwdArgs {
+    const uint16_t* x;
+    const uint16_t* w;
+    const uint16_t* bias;
+    uint16_t* z;         // [N][P][Q][K] fp16 pre-activation, or NULL
+    uint16_t* y;         // [N][P][Q][K] fp16 output
+    uint32_t x_bytes;
+    uint32_t w_bytes;
+    uint32_t y_bytes;    // also the size of z
+    int N, H, W, C, K, R, S, P, Q, stride, pad, act;
+    int npq;             // N*P*Q
+    int tiles_m, tiles_n;
+    int csteps;          // ceil(C / 64)
+    FastDiv div_pq;
+    FastDiv div_q;
+};
+
+struct FwdConfig {
+    int BM, BN, WM, WN;
+    const char* name;
+};
+int fwd_num_configs();
+const FwdConfig& fwd_config(int id);
+hipError_t launch_fwd(int id, const FwdArgs& a, hipStream_t stream);
+int fwd_private_bytes(int id);
+
 int num_tile_configs();
 const TileConfig& tile_config(int id);
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);

@@ -1353,4 +1353,265 @@ int wgrad_private_bytes(int id)
     return (id >= 0 && id < kNumWgradConfigs) ? kWgradPrivate[id]() : -1;
 }
 
+// ================================================================== forward
+//
+// The forward layer with the fused bias + activation epilogue:
+//   z[m,k] = bias[k] + sum over taps (r,t) and c of x[n, p*s-pad+r, q*s-pad+t, c] * w[k,r,t,c]
+//   y[m,k] = hardswish(z) (act 1) or z (act 0), for output pixel m = (n,p,q).
+// GEMM D[k][m] with A = w (rows = output channels k, reduction c) and B =
+// x_tap^T (columns = output pixels, reduction c). Both slices are
+// [rows][64 channels] tiles of 128-byte rows in LDS, loaded like dgrad's dy
+// slice, and both fragments are single ds_read_b128 (8 consecutive c of one
+// row). Slices go tap by tap and, within a tap, over C in 64-wide steps; a
+// lane's x offset and padding check change only at tap boundaries.
+
+namespace {
+
+// hardswish(z) = z * min(max(z + 3, 0), 6) / 6, in fp32
+__device__ inline float hardswish_f(float z)
+{
+    return z * fminf(fmaxf(z + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN) fwd_igemm(FwdArgs a)
+{
+    constexpr int BK = 64;
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;     // wave tile: TM pixels x TN output channels
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int X_BYTES = BM * 128, W_BYTES = BN * 128;
+    constexpr int STAGE = X_BYTES + W_BYTES;
+    constexpr int X_INSTR = X_BYTES / 1024 / NW, W_INSTR = W_BYTES / 1024 / NW;
+    constexpr int LD = X_INSTR + W_INSTR;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(X_BYTES % (1024 * NW) == 0 && W_BYTES % (1024 * NW) == 0, "whole 1 KiB blocks per wave");
+    static_assert(3 * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(2 * LD < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) char lds[3 * STAGE];
+    const uint32_t lds_u32 = (uint32_t)(uintptr_t)((lds_char*)lds);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM;
+    const int wn = wave / WM;
+
+    const int tn_ = pin((int)(blockIdx.x % (uint32_t)a.tiles_n));
+    const int tm_ = pin((int)(blockIdx.x / (uint32_t)a.tiles_n));
+    const int m0 = pin(tm_ * BM);
+    const int n0 = pin(tn_ * BN);
+    const int C = pin(a.C);
+    const int K = pin(a.K);
+    const int Hh = pin(a.H), Ww = pin(a.W);
+    const int S = pin(a.S);
+    const int csteps = pin(a.csteps);
+    const int ns = a.R * S * csteps;
+    const i32x4 x_desc = raw_descriptor(a.x, a.x_bytes);
+    const i32x4 w_desc = raw_descriptor(a.w, a.w_bytes);
+
+    // Lane geometry: block b = j*NW + wave of a slice covers rows 8b..8b+7;
+    // lane l fills row 8b + l/8 at chunk position l%8, holding logical chunk
+    // (l%8) ^ dy_swizzle(row).
+    uint32_t x_base[X_INSTR];   // element offset of the row's pixel at tap (0,0), modulo 2^32
+    int x_h0[X_INSTR], x_w0[X_INSTR];
+    int x_ch[X_INSTR];
+    uint32_t x_vo[X_INSTR];     // the lane's byte offset for the current tap (2^31: outside)
+#pragma unroll
+    for (int j = 0; j < X_INSTR; ++j) {
+        const int row = (j * NW + wave) * 8 + (lane >> 3);
+        x_ch[j] = ((lane & 7) ^ dy_swizzle(row)) * 8;
+        const int m = m0 + row;
+        const uint32_t n = fastdiv((uint32_t)m, a.div_pq);
+        const uint32_t rem = (uint32_t)m - n * a.div_pq.d;
+        const uint32_t p = fastdiv(rem, a.div_q);
+        const uint32_t q = rem - p * a.div_q.d;
+        x_h0[j] = m < a.npq ? (int)p * a.stride - a.pad : -(1 << 24);   // a dead row fails every h >= 0 test
+        x_w0[j] = (int)q * a.stride - a.pad;
+        x_base[j] = ((n * (uint32_t)Hh + (uint32_t)x_h0[j]) * (uint32_t)Ww + (uint32_t)x_w0[j]) * (uint32_t)C + (uint32_t)x_ch[j];
+    }
+    uint32_t w_lane[W_INSTR];   // byte offset of the lane's filter chunk at tap (0,0), c0 = 0 (2^31: k >= K)
+    int w_ch[W_INSTR];
+#pragma unroll
+    for (int j = 0; j < W_INSTR; ++j) {
+        const int row = (j * NW + wave) * 8 + (lane >> 3);
+        w_ch[j] = ((lane & 7) ^ dy_swizzle(row)) * 8;
+        const int k = n0 + row;
+        w_lane[j] = k < K ? (uint32_t)(k * a.R * S * C + w_ch[j]) * 2u : 0x80000000u;
+    }
+
+    // request cursor: tap (r, t) and channel step c0
+    int rq_r = 0, rq_t = 0, rq_c0 = 0;
+    bool new_tap = true;
+    uint32_t w_tap = 0;
+    auto issue = [&](int st) {
+        if (new_tap) {
+            new_tap = false;
+            const uint32_t tapoff = (uint32_t)(rq_r * Ww + rq_t) * (uint32_t)C;
+#pragma unroll
+            for (int j = 0; j < X_INSTR; ++j) {
+                const bool ok = ((unsigned)(x_h0[j] + rq_r) < (unsigned)Hh) & ((unsigned)(x_w0[j] + rq_t) < (unsigned)Ww);
+                x_vo[j] = ok ? (x_base[j] + tapoff) * 2u : 0x80000000u;
+            }
+            w_tap = (uint32_t)((rq_r * S + rq_t) * C) * 2u;
+        }
+        const uint32_t base = lds_u32 + (uint32_t)(st * STAGE);
+#pragma unroll
+        for (int j = 0; j < X_INSTR; ++j) {
+            const uint32_t vo = rq_c0 + x_ch[j] >= C ? 0x80000000u : x_vo[j];
+            dma16(x_desc, vo, (uint32_t)rq_c0 * 2u, base + (uint32_t)((j * NW + wave) * 1024));
+        }
+#pragma unroll
+        for (int j = 0; j < W_INSTR; ++j) {
+            const uint32_t vo = rq_c0 + w_ch[j] >= C ? 0x80000000u : w_lane[j];
+            dma16(w_desc, vo, w_tap + (uint32_t)rq_c0 * 2u, base + (uint32_t)(X_BYTES + (j * NW + wave) * 1024));
+        }
+        rq_c0 += BK;
+        if (rq_c0 >= C) {
+            rq_c0 = 0;
+            new_tap = true;
+            if (++rq_t == S) {
+                rq_t = 0;
+                ++rq_r;
+            }
+        }
+    };
+
+    // fragments: row (lane % 32) of each 32-row block, chunk 2*kk + lane/32
+    const int xr0 = wm * TM + (lane & 31);
+    const int wr0 = wn * TN + (lane & 31);
+    const int x_sw = dy_swizzle(xr0), w_sw = dy_swizzle(wr0);   // the same for every block (32 keeps bits 1..3)
+    float16_t acc[FN][FM];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[fn][fm][e] = 0.0f;
+    auto compute = [&](int st) {
+        const int sb = st * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            half8_t af[FN], bf[FM];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                af[fn] = __builtin_bit_cast(half8_t, *(const u32x4*)(lds + sb + X_BYTES + (wr0 + fn * 32) * 128 +
+                                                                    (((kk * 2 + (lane >> 5)) ^ w_sw) * 16)));
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                bf[fm] = __builtin_bit_cast(half8_t, *(const u32x4*)(lds + sb + (xr0 + fm * 32) * 128 +
+                                                                    (((kk * 2 + (lane >> 5)) ^ x_sw) * 16)));
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[fn], bf[fm], acc[fn][fm], 0, 0, 0);
+        }
+    };
+
+    if (ns > 0)
+        issue(0);
+    if (ns > 1)
+        issue(1);
+    for (int i = 0; i < ns; ++i) {
+        if (i + 1 < ns)
+            wait_vmcnt<LD>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();        // every wave's part of slice i is in LDS, and every wave
+                                // is done with the stage the next request reuses
+        if (i + 2 < ns)
+            issue((i + 2) % 3);
+        compute(i % 3);
+    }
+
+    // epilogue: the lane holds output channels 8*gq + 4*(lane/32) .. +3 of
+    // block fn, pixel lane%32 of block fm; z = acc + bias, y = act(z), each
+    // rounded once to fp16 and stored as 8 bytes
+    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(a.y, a.y_bytes);
+    const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(a.z != nullptr ? a.z : a.y, a.y_bytes);
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(a.bias, (uint32_t)K * 2u);
+    const bool store_z = a.z != nullptr;
+    const bool hs = a.act == 1;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int k = n0 + wn * TN + fn * 32 + 8 * gq + 4 * (lane >> 5);
+            const bool kbad = k >= K;
+            const u32x2 braw = __builtin_amdgcn_raw_buffer_load_b64(b_rsrc, out_of_range_if((uint32_t)kbad, (uint32_t)k * 2u), 0, 0);
+            const half4_t bh = __builtin_bit_cast(half4_t, braw);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int m = m0 + wm * TM + fm * 32 + (lane & 31);
+                const uint32_t bad = (uint32_t)kbad | (uint32_t)(m >= a.npq);
+                const uint32_t off = ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 2u;
+                float zv[4], yv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    zv[i] = acc[fn][fm][4 * gq + i] + (float)bh[i];
+                    yv[i] = hs ? hardswish_f(zv[i]) : zv[i];
+                }
+                const half4_t zo{(_Float16)zv[0], (_Float16)zv[1], (_Float16)zv[2], (_Float16)zv[3]};
+                const half4_t yo{(_Float16)yv[0], (_Float16)yv[1], (_Float16)yv[2], (_Float16)yv[3]};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yo), y_rsrc, out_of_range_if(bad, off), 0, 0);
+                if (store_z)
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, zo), z_rsrc, out_of_range_if(bad, off), 0, 0);
+            }
+        }
+}
+
+// The compiled forward tile configurations: (BM, BN, WM, WN).
+#define CBW_FWD_CONFIGS(X) \
+    X(256, 128, 4, 2)      \
+    X(128, 128, 2, 2)      \
+    X(128, 64, 2, 2)
+
+#define CBW_FWD_ENTRY(BM, BN, WM, WN) {BM, BN, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN},
+const FwdConfig kFwdConfigs[] = {CBW_FWD_CONFIGS(CBW_FWD_ENTRY)};
+constexpr int kNumFwdConfigs = sizeof(kFwdConfigs) / sizeof(kFwdConfigs[0]);
+
+template <int BM, int BN, int WM, int WN>
+hipError_t fwd_launch(const FwdArgs& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((fwd_igemm<BM, BN, WM, WN>), dim3(a.tiles_m * a.tiles_n), dim3(64 * WM * WN), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+int fwd_private(void)
+{
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fwd_igemm<BM, BN, WM, WN>)) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return (int)attr.localSizeBytes;
+}
+
+using FwdLaunchFn = hipError_t (*)(const FwdArgs&, hipStream_t);
+#define CBW_FWD_LAUNCH(BM, BN, WM, WN) &fwd_launch<BM, BN, WM, WN>,
+#define CBW_FWD_PRIVATE(BM, BN, WM, WN) &fwd_private<BM, BN, WM, WN>,
+const FwdLaunchFn kFwdLaunch[] = {CBW_FWD_CONFIGS(CBW_FWD_LAUNCH)};
+int (*const kFwdPrivate[])(void) = {CBW_FWD_CONFIGS(CBW_FWD_PRIVATE)};
+
+}  // namespace
+
+int fwd_num_configs() { return kNumFwdConfigs; }
+
+const FwdConfig& fwd_config(int id) { return kFwdConfigs[id]; }
+
+hipError_t launch_fwd(int id, const FwdArgs& a, hipStream_t stream)
+{
+    if (id < 0 || id >= kNumFwdConfigs)
+        return hipErrorInvalidValue;
+    return kFwdLaunch[id](a, stream);
+}
+
+int fwd_private_bytes(int id)
+{
+    return (id >= 0 && id < kNumFwdConfigs) ? kFwdPrivate[id]() : -1;
+}
+
 }  // namespace cbw

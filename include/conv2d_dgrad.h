@@ -235,6 +235,44 @@ int conv2d_wgrad_check(const void* dy, const void* x, void* dw,
                        int N, int H, int W, int C, int K, int R, int S,
                        int stride, int pad);
 
+/*
+ * The forward layer with the fused bias + activation epilogue that the
+ * Bolt paper notes (KuangjuX/Paper-reading #28, "Insights") describe as
+ * Conv2D + BiasAdd + Hardswish:
+ *
+ *   z[n,p,q,k] = bias[k] + sum over r,t,c of x[n, p*s - pad + r, q*s - pad + t, c] * w[k,r,t,c]
+ *   y = hardswish(z) = z * min(max(z + 3, 0), 6) / 6   (act = 1), or y = z (act = 0),
+ *
+ * accumulated in fp32; z and y are each rounded once to fp16. z is the saved
+ * pre-activation that conv2d_dgrad_nhwc's fused epilogue consumes.
+ *
+ * Arguments:
+ *   x    [N][H][W][C]   fp16 NHWC input
+ *   w    [K][R][S][C]   fp16 filter
+ *   bias [K]            fp16 (8-byte aligned)
+ *   z    [N][P][Q][K]   fp16 pre-activation output, or NULL not to store it
+ *   y    [N][P][Q][K]   fp16 output
+ * Shapes, limits and status codes are those of conv2d_dgrad_nhwc; y and z
+ * must not overlap the inputs or each other. No workspace; asynchronous on
+ * `stream`.
+ */
+int conv2d_forward_nhwc(const void* x, const void* w, const void* bias, void* z, void* y,
+                        int N, int H, int W, int C, int K, int R, int S,
+                        int stride, int pad, int act, void* stream);
+
+/* The same with an explicit tile configuration (0 .. conv2d_forward_num_configs()-1). */
+int conv2d_forward_nhwc_config(const void* x, const void* w, const void* bias, void* z, void* y,
+                               int N, int H, int W, int C, int K, int R, int S,
+                               int stride, int pad, int act, int config_id, void* stream);
+
+/* Number of compiled forward tile configurations. */
+int conv2d_forward_num_configs(void);
+
+/* Validation alone (no HIP call) for conv2d_forward_nhwc. */
+int conv2d_forward_check(const void* x, const void* w, const void* bias, void* z, void* y,
+                         int N, int H, int W, int C, int K, int R, int S,
+                         int stride, int pad, int act);
+
 /* Thread-local text of the last error ("" if none). */
 const char* conv2d_dgrad_last_error(void);
 

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "conv2d_dgrad.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(conv2d_[dw]grad_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(conv2d_(?:dgrad|wgrad|forward)_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -118,6 +118,43 @@ def test_wgrad_configs_and_bad_calls():
     assert e.value.code == cb.UNSUPPORTED
     with pytest.raises(cb.DgradError) as e:
         cb.conv2d_wgrad_nhwc_config(DY, DX, WP, 2, 8, 8, 16, 8, 3, 3, 1, 1, config_id=99, stream=0)
+    assert e.value.code == cb.INVALID_ARGUMENT
+
+
+FB = 0x50000000   # bias
+FG = dict(N=2, H=8, W=8, C=16, K=8, R=3, S=3, stride=2, pad=1)
+
+
+def fcheck(x=DX, w=WP, bias=FB, z=Z, y=DY, act=1, **kw):
+    args = dict(FG)
+    args.update(kw)
+    return cb.conv2d_forward_check(x, w, bias, z, y, args["N"], args["H"], args["W"], args["C"], args["K"],
+                                   args["R"], args["S"], args["stride"], args["pad"], act)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, cb.OK), ({"z": 0}, cb.OK),                                 # z is optional
+    ({"act": 2}, cb.INVALID_ARGUMENT), ({"act": -1}, cb.INVALID_ARGUMENT),
+    ({"x": 0}, cb.INVALID_ARGUMENT), ({"w": 0}, cb.INVALID_ARGUMENT), ({"bias": 0}, cb.INVALID_ARGUMENT),
+    ({"y": 0}, cb.INVALID_ARGUMENT),
+    ({"y": DY + 8}, cb.INVALID_ARGUMENT), ({"bias": FB + 4}, cb.INVALID_ARGUMENT),   # misaligned
+    ({"y": DX + 16}, cb.INVALID_ARGUMENT),                          # y overlaps x
+    ({"z": DY + 16}, cb.INVALID_ARGUMENT),                          # z overlaps y
+    ({"C": 12}, cb.UNSUPPORTED), ({"K": 4}, cb.UNSUPPORTED), ({"N": 0}, cb.INVALID_ARGUMENT),
+])
+def test_forward_validation_codes(kw, code):
+    assert fcheck(**kw) == code
+    if code != cb.OK:
+        assert cb.conv2d_dgrad_last_error() != ""
+
+
+def test_forward_configs_and_bad_calls():
+    assert cb.conv2d_forward_num_configs() >= 2
+    with pytest.raises(cb.DgradError) as e:
+        cb.conv2d_forward_nhwc(DX, WP, FB, Z, DY, 2, 8, 8, 12, 8, 3, 3, 1, 1, 1, stream=0)
+    assert e.value.code == cb.UNSUPPORTED
+    with pytest.raises(cb.DgradError) as e:
+        cb.conv2d_forward_nhwc_config(DX, WP, FB, Z, DY, 2, 8, 8, 16, 8, 3, 3, 1, 1, 1, config_id=99, stream=0)
     assert e.value.code == cb.INVALID_ARGUMENT
 
 
