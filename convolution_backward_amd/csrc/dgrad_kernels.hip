@@ -1528,38 +1528,69 @@ __global__ void __launch_bounds__(64 * WM * WN) fwd_igemm(FwdArgs a)
 
     // epilogue: the lane holds output channels 8*gq + 4*(lane/32) .. +3 of
     // block fn, pixel lane%32 of block fm; z = acc + bias, y = act(z), each
-    // rounded once to fp16 and stored as 8 bytes
+    // rounded once to fp16. Each wave's 32 pixels x TN channels pass through
+    // LDS (chunk q of staged row p at position q ^ ((p >> 1) % CH)) and go out
+    // as 16-byte chunks, so that one store covers 64/CH whole pixel rows of the
+    // wave's TN*2 bytes; first z, then y.
+    constexpr int CH = TN / 8;             // 16-byte chunks per staged pixel row
+    constexpr int EROW = TN * 2;
+    constexpr int EBLK = 32 * EROW;
+    constexpr int PPI = 64 / CH;           // pixels per store instruction
+    constexpr int EST = 32 / PPI;          // store instructions per pixel block
+    static_assert(NW * EBLK <= 3 * STAGE, "the staging blocks fit in LDS");
+    static_assert(CH >= 2 && CH <= 64 && 64 % CH == 0, "whole pixel rows per store");
+    __syncthreads();                       // no wave reads a slice any more (every load has landed)
     const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(a.y, a.y_bytes);
     const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(a.z != nullptr ? a.z : a.y, a.y_bytes);
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(a.bias, (uint32_t)K * 2u);
     const bool store_z = a.z != nullptr;
     const bool hs = a.act == 1;
+    lds_char* blk = (lds_char*)lds + wave * EBLK;
+    half4_t bh[FN][4];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int k = n0 + wn * TN + fn * 32 + 8 * gq + 4 * (lane >> 5);
-            const bool kbad = k >= K;
-            const u32x2 braw = __builtin_amdgcn_raw_buffer_load_b64(b_rsrc, out_of_range_if((uint32_t)kbad, (uint32_t)k * 2u), 0, 0);
-            const half4_t bh = __builtin_bit_cast(half4_t, braw);
+            bh[fn][gq] = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                         b_rsrc, out_of_range_if((uint32_t)(k >= K), (uint32_t)k * 2u), 0, 0));
+        }
+    const int cw = n0 + wn * TN;           // first output channel of this wave's block
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = m0 + wm * TM + fm * 32 + (lane & 31);
-                const uint32_t bad = (uint32_t)kbad | (uint32_t)(m >= a.npq);
-                const uint32_t off = ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 2u;
-                float zv[4], yv[4];
+    for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    zv[i] = acc[fn][fm][4 * gq + i] + (float)bh[i];
-                    yv[i] = hs ? hardswish_f(zv[i]) : zv[i];
+        for (int out = 0; out < 2; ++out) {
+            if (out == 0 && !store_z)
+                continue;
+            const int pw = lane & 31;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float zv = acc[fn][fm][4 * gq + i] + (float)bh[fn][gq][i];
+                        v[i] = (out == 1 && hs) ? hardswish_f(zv) : zv;
+                    }
+                    const half4_t o{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                    const int q = fn * 4 + gq;
+                    *(__attribute__((address_space(3))) u32x2*)(blk + pw * EROW + ((q ^ ((pw >> 1) % CH)) * 16) + (lane >> 5) * 8) =
+                        __builtin_bit_cast(u32x2, o);
                 }
-                const half4_t zo{(_Float16)zv[0], (_Float16)zv[1], (_Float16)zv[2], (_Float16)zv[3]};
-                const half4_t yo{(_Float16)yv[0], (_Float16)yv[1], (_Float16)yv[2], (_Float16)yv[3]};
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yo), y_rsrc, out_of_range_if(bad, off), 0, 0);
-                if (store_z)
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, zo), z_rsrc, out_of_range_if(bad, off), 0, 0);
+#pragma unroll
+            for (int e = 0; e < EST; ++e) {
+                const int pr = e * PPI + lane / CH;
+                const int q = lane % CH;
+                const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(blk + pr * EROW + ((q ^ ((pr >> 1) % CH)) * 16));
+                const int m = m0 + wm * TM + fm * 32 + pr;
+                const int c = cw + q * 8;
+                const uint32_t bad = (uint32_t)(m >= a.npq) | (uint32_t)(c >= K);
+                const uint32_t off = ((uint32_t)m * (uint32_t)K + (uint32_t)c) * 2u;
+                __builtin_amdgcn_raw_buffer_store_b128(v, out == 0 ? z_rsrc : y_rsrc, out_of_range_if(bad, off), 0, kStoreNT);
             }
         }
+    }
 }
 
 // The compiled forward tile configurations: (BM, BN, WM, WN).
