@@ -109,3 +109,29 @@ def test_forward_measured_layer(idx):
     assert_close(y.reshape(-1, cfg.K)[rows], yr, f"{cfg.name} y")
     z2, y2 = run_forward(cfg, x, w, b, 1)
     assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
+# x just below the 2^30-element limit (1x1 and strided 3x3), small-integer
+# inputs: z is exact and must equal the oracle's RNE fp16 value bit for bit
+# on sampled output pixels, including the last ones.
+MAX_SHAPES = [
+    ("x_1x1_s1", (63, 128, 128, 1024, 64, 1, 1, 1, 0)),       # x 1,056,964,608 elements
+    ("x_3x3_s2", (40, 448, 448, 128, 64, 3, 3, 2, 1)),        # x 1,027,604,480 elements
+]
+
+
+@pytest.mark.parametrize("name,shape", MAX_SHAPES, ids=[n for n, _ in MAX_SHAPES])
+def test_forward_maximum_sizes_bit_exact(name, shape):
+    cfg = small_config(*shape, name=name)
+    assert cfg.N * cfg.H * cfg.W * cfg.C < 2 ** 30
+    rng = np.random.Generator(np.random.PCG64(57))
+    x = rng.integers(-2, 3, size=(cfg.N, cfg.H, cfg.W, cfg.C), dtype=np.int8).astype(np.float16)
+    w = rng.integers(-2, 3, size=(cfg.K, cfg.R, cfg.S, cfg.C), dtype=np.int8).astype(np.float16)
+    b = rng.integers(-4, 5, size=cfg.K).astype(np.float16)
+    note(f"forward maximum size {name} {shape}")
+    z, y = run_forward(cfg, x, w, b, 1)
+    npq = cfg.N * cfg.P * cfg.Q
+    rows = np.unique(np.concatenate([rng.choice(npq, size=300, replace=False), np.arange(npq - 64, npq)]))
+    zr, yr = oracle.forward(x, w, b, cfg.stride, cfg.pad, act=1, rows=rows)
+    assert np.array_equal(z.reshape(-1, cfg.K)[rows], oracle.round_to_half(zr))
+    assert_close(y.reshape(-1, cfg.K)[rows], yr, f"{name} y")

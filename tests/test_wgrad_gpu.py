@@ -118,3 +118,34 @@ def test_wgrad_side_stream():
     ref, mag = oracle.wgrad(dy, x, cfg.R, cfg.S, cfg.stride, cfg.pad, with_abs=True)
     note("wgrad side stream")
     assert_wgrad_close(run_wgrad(cfg, dy, x, stream=torch.cuda.Stream()), ref, mag, "side stream")
+
+
+# One tensor just below the 2^30-element limit in each case (x of a 1x1 layer
+# and of a strided 3x3 layer), so byte offsets near 2^31 and the last pixels
+# of the reduction are exercised. Small-integer inputs keep every sum exact
+# (each filter element sums at most ~10^6 products of magnitude <= 4, far
+# below 2^24), so sampled filter rows must match the oracle bit for bit.
+MAX_SHAPES = [
+    ("x_1x1_s1", (63, 128, 128, 1024, 64, 1, 1, 1, 0)),       # x 1,056,964,608 elements
+    ("x_3x3_s2", (40, 448, 448, 128, 64, 3, 3, 2, 1)),        # x 1,027,604,480 elements
+]
+
+
+def _int8(rng, shape):
+    return rng.integers(-2, 3, size=shape, dtype=np.int8).astype(np.float16)
+
+
+@pytest.mark.parametrize("name,shape", MAX_SHAPES, ids=[n for n, _ in MAX_SHAPES])
+def test_wgrad_maximum_sizes_bit_exact(name, shape):
+    cfg = small_config(*shape, name=name)
+    assert cfg.N * cfg.H * cfg.W * cfg.C < 2 ** 30
+    rng = np.random.Generator(np.random.PCG64(47))
+    dy = _int8(rng, (cfg.N, cfg.P, cfg.Q, cfg.K))
+    x = _int8(rng, (cfg.N, cfg.H, cfg.W, cfg.C))
+    note(f"wgrad maximum size {name} {shape}")
+    got = run_wgrad(cfg, dy, x)
+    assert not np.isnan(got).any()
+    nrow = cfg.K * cfg.R * cfg.S
+    rows = np.array(sorted({0, nrow // 2, nrow - 1}))
+    ref = oracle.wgrad(dy, x, cfg.R, cfg.S, cfg.stride, cfg.pad, rows=rows)
+    assert np.array_equal(got.reshape(-1, cfg.C)[rows].astype(np.float64), ref)
