@@ -1266,9 +1266,22 @@ __global__ void __launch_bounds__(256) wgrad_reduce(WgradArgs a)
         return;
     const int tile = (int)(u / GROUPS);
     const int gq = (int)(u % GROUPS);
+    // eight loads in flight at a time; the adds stay in split order
+    const float* src = a.part + ((size_t)tile * (size_t)GROUPS + (size_t)gq) * 4;
+    const size_t split_stride = (size_t)a.tiles * (size_t)GROUPS * 4;
     float4_t sum{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int sp = 0; sp < a.splits; ++sp)
-        sum += *(const float4_t*)(a.part + (((size_t)sp * (size_t)a.tiles + (size_t)tile) * (size_t)GROUPS + (size_t)gq) * 4);
+    int sp = 0;
+    for (; sp + 8 <= a.splits; sp += 8) {
+        float4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = *(const float4_t*)(src + (size_t)(sp + u) * split_stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            sum += v[u];
+    }
+    for (; sp < a.splits; ++sp)
+        sum += *(const float4_t*)(src + (size_t)sp * split_stride);
     const int gi = gq / NT;
     const int th = gq % NT;
     const int wave = th / 64, lane = th % 64;
