@@ -113,6 +113,8 @@ def main():
                     help="timed wgrad (filter gradient) calls per layer, after the dgrad timing (0 skips)")
     ap.add_argument("--forward-reps", type=int, default=10,
                     help="timed forward (conv + bias + hardswish) calls per layer shape, after the rest (0 skips)")
+    ap.add_argument("--chain-reps", type=int, default=10,
+                    help="timed calls of the fused two-step chain and of the unfused pair, after the rest (0 skips)")
     ap.add_argument("--only", default="",
                     help="comma-separated layer names: time only these (for profiler runs)")
     ap.add_argument("--copy-calibrate-mb", type=float, default=0.0,
@@ -326,6 +328,63 @@ def main():
                "value": sum(cfg.useful_flops() for cfg, _ in layers) / fsum / 1e12, "unit": "TFLOP/s",
                "layers": flayers}
 
+    # ---- persistent fusion (a NEXT row): the stage-2 bottleneck's 3x3 dgrad,
+    # hardswish', then the 1x1 dgrad, fused in one kernel, against the same two
+    # steps as two calls of this library (t stored in fp16 between them); not
+    # part of `value`
+    chain = None
+    if args.chain_reps > 0 and not args.only:
+        from workloads import CHAIN_BY_NAME, make_chain_inputs
+        ccfg = CHAIN_BY_NAME["r50_stage2_chain_3x3_1x1_n256"]
+        ci = {k: (None if v is None else torch.from_numpy(v).to(dev)) for k, v in make_chain_inputs(ccfg).items()}
+        cdx = torch.empty((ccfg.N, ccfg.H, ccfg.W, ccfg.C), dtype=torch.float16, device=dev)
+        ct = torch.empty((ccfg.N, ccfg.H, ccfg.W, ccfg.Cm), dtype=torch.float16, device=dev)
+        cdx2 = torch.empty_like(cdx)
+
+        def fused():
+            cb.conv2d_dgrad_chain_nhwc(ci["dy"], ci["w1"], ci["z"], ci["w2"], cdx, ccfg.N, ccfg.H, ccfg.W, ccfg.Cm,
+                                       ccfg.K, ccfg.R, ccfg.S, ccfg.pad, ccfg.C, ccfg.epilogue, stream.cuda_stream)
+
+        def pair():
+            cb.conv2d_dgrad_nhwc(ci["dy"], ci["w1"], ct, ccfg.N, ccfg.H, ccfg.W, ccfg.Cm, ccfg.K, ccfg.R, ccfg.S, 1,
+                                 ccfg.pad, ccfg.epilogue, ci["z"], stream.cuda_stream)
+            cb.conv2d_dgrad_nhwc(ct, ci["w2"], cdx2, ccfg.N, ccfg.H, ccfg.W, ccfg.C, ccfg.Cm, 1, 1, 1, 0,
+                                 cb.EPI_NONE, None, stream.cuda_stream)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.chain_reps)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+            return float(np.mean(ms)), float(np.min(ms))
+
+        f_avg, f_min = timed(fused)
+        p_avg, p_min = timed(pair)
+        fl = ccfg.useful_flops()
+        nbytes = ccfg.algorithmic_bytes()
+        t_bytes = 2 * 2 * ccfg.N * ccfg.H * ccfg.W * ccfg.Cm     # t written and read back by the pair
+        if fl / nbytes >= RIDGE:
+            rl = {"bound": "mfma", "achieved": fl / (f_avg * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        else:
+            rl = {"bound": "hbm", "achieved": nbytes / (f_avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        rl["frac"] = rl["achieved"] / rl["peak"]
+        chain = {"note": "dx = dgrad_1x1(fp16(dgrad_3x3(dy, w1) * hardswish'(z)), w2), ResNet-50 stage-2 bottleneck "
+                         "(3x3 64->64 and 1x1 256->64 convolutions) at N=256, seeded synthetic; fused = one kernel "
+                         "with the intermediate tile in LDS, pair = two dgrad calls with t in HBM",
+                 "workload": ccfg.name, "fused_us": f_avg * 1e3, "fused_min_us": f_min * 1e3,
+                 "pair_us": p_avg * 1e3, "pair_min_us": p_min * 1e3, "speedup": p_avg / f_avg,
+                 "tflops": fl / (f_avg * 1e-3) / 1e12, "alg_mb": nbytes / 1e6,
+                 "pair_alg_mb": (nbytes + t_bytes) / 1e6, "roofline": rl}
+        log(f"[chain] {ccfg.name:34s} fused {f_avg*1e3:9.2f} us  pair {p_avg*1e3:9.2f} us  "
+            f"{chain['tflops']:7.1f} TFLOP/s  {rl['bound']} {rl['frac']:.1%}")
+        del ci, cdx, ct, cdx2
+
     flops = sum(cfg.useful_flops() for cfg, _ in layers)
     kernel_ms = sum(p["avg_us"] for p in per_layer) / 1e3
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -369,6 +428,7 @@ def main():
         "cold": cold,
         "wgrad": wgrad,
         "forward": fwd,
+        "chain": chain,
         "device": torch.cuda.get_device_name(dev),
         "build": cb.conv2d_dgrad_build_info(),
     }

@@ -66,6 +66,8 @@ def _bind(lib):
     lib.conv2d_forward_nhwc_config.argtypes = [vp] * 5 + [i] * 10 + [i, vp]
     lib.conv2d_forward_num_configs.argtypes = []
     lib.conv2d_forward_check.argtypes = [vp] * 5 + [i] * 10
+    lib.conv2d_dgrad_chain_nhwc.argtypes = [vp] * 5 + [i] * 10 + [vp]
+    lib.conv2d_dgrad_chain_check.argtypes = [vp] * 5 + [i] * 10
     lib.conv2d_dgrad_last_error.argtypes = []
     lib.conv2d_dgrad_last_error.restype = ctypes.c_char_p
     lib.conv2d_dgrad_build_info.argtypes = []
@@ -76,7 +78,7 @@ def _bind(lib):
                  "conv2d_dgrad_cache_load", "conv2d_dgrad_plan", "conv2d_dgrad_check",
                  "conv2d_wgrad_nhwc", "conv2d_wgrad_nhwc_config", "conv2d_wgrad_num_configs", "conv2d_wgrad_check",
                  "conv2d_forward_nhwc", "conv2d_forward_nhwc_config", "conv2d_forward_num_configs",
-                 "conv2d_forward_check"):
+                 "conv2d_forward_check", "conv2d_dgrad_chain_nhwc", "conv2d_dgrad_chain_check"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -236,6 +238,41 @@ def forward(x, w, bias, stride, pad, act=ACT_HARDSWISH, with_z=True, config_id=N
     else:
         conv2d_forward_nhwc_config(x, w, bias, z, y, N, H, W, C, K, R, S, stride, pad, act, config_id)
     return z, y
+
+
+def conv2d_dgrad_chain_nhwc(dy, w1, z, w2, dx, N, H, W, Cm, K, R, S, pad, C, epilogue=EPI_NONE, stream=None):
+    """Two dgrad steps of a bottleneck in one kernel: t = fp16(dgrad(dy, w1) * g(z))
+    at stride 1, then dx = t @ w2 (the 1x1 step), enqueued on `stream`."""
+    return _check(get_lib().conv2d_dgrad_chain_nhwc(_ptr(dy), _ptr(w1), _ptr(z), _ptr(w2), _ptr(dx), N, H, W, Cm, K,
+                                                    R, S, pad, C, epilogue, _stream(stream, dy, dx)))
+
+
+def conv2d_dgrad_chain_check(dy, w1, z, w2, dx, N, H, W, Cm, K, R, S, pad, C, epilogue=EPI_NONE) -> int:
+    """Validation alone; returns the status code (no exception)."""
+    return get_lib().conv2d_dgrad_chain_check(_ptr(dy), _ptr(w1), _ptr(z), _ptr(w2), _ptr(dx), N, H, W, Cm, K, R, S,
+                                              pad, C, epilogue)
+
+
+def dgrad_chain(dy, w1, z, w2, pad, epilogue=EPI_NONE, out=None):
+    """Allocate dx [N,H,W,C] float16 with torch.empty (unless `out` is given)
+    and fill it on the current stream with the fused chain.
+
+    dy [N,P,Q,K], w1 [K,R,S,Cm], z [N,H,W,Cm] (or None for EPI_NONE) and
+    w2 [Cm,1,1,C] are float16 GPU tensors; H = P - 2*pad + R - 1 (stride 1).
+    """
+    import torch
+    for name, t in (("dy", dy), ("w1", w1), ("w2", w2)) + ((("z", z),) if z is not None else ()):
+        if t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
+    N, P, Q, K = dy.shape
+    K2, R, S, Cm = w1.shape
+    if K2 != K or w2.shape[0] != Cm or w2.dim() != 4 or tuple(w2.shape[1:3]) != (1, 1):
+        raise ValueError("dy, w1 and w2 [Cm,1,1,C] disagree on K or Cm")
+    C = w2.shape[3]
+    H, W = P - 2 * pad + R - 1, Q - 2 * pad + S - 1
+    dx = out if out is not None else torch.empty((N, H, W, C), dtype=torch.float16, device=dy.device)
+    conv2d_dgrad_chain_nhwc(dy, w1, z, w2, dx, N, H, W, Cm, K, R, S, pad, C, epilogue)
+    return dx
 
 
 def conv2d_dgrad_num_configs() -> int:

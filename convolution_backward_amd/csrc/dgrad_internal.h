@@ -181,6 +181,29 @@ const FwdConfig& fwd_config(int id);
 hipError_t launch_fwd(int id, const FwdArgs& a, hipStream_t stream);
 int fwd_private_bytes(int id);
 
+// ------------------------------------------------------------------ chain
+
+// Two dgrad steps of a bottleneck in one kernel (see chain_igemm in
+// chain_kernels.hip): t[m,c] = fp16(g(z[m,c]) * stride-1 dgrad of dy through
+// the RxS filter w1 [K][R][S][Cm]), then dx[m,ci] = fp16(sum over c of
+// t[m,c] * w2[c,ci]) with the 1x1 filter w2 [Cm][C]; t stays in LDS.
+struct ChainArgs {
+    const uint16_t* dy;  // [N][P][Q][K]
+    const uint16_t* w1;  // [K][R][S][Cm]
+    const uint16_t* z;   // [N][H][W][Cm] (read for epi 1 and 2)
+    const uint16_t* w2;  // [Cm][C]
+    uint16_t* dx;        // [N][H][W][C]
+    uint32_t dy_bytes, w1_bytes, z_bytes, w2_bytes, dx_bytes;
+    int N, H, W, Cm, K, R, S, pad, P, Q, C, epi;
+    int M;               // N*H*W
+    int tiles;           // ceil(M / 128)
+    FastDiv div_hw;      // division by H*W
+    FastDiv div_w;       // division by W
+};
+hipError_t launch_chain(const ChainArgs& a, hipStream_t stream);
+int chain_private_bytes(int Cm, int epi);   // scratch bytes per lane, -1 if unknown
+int chain_lds_bytes(int Cm);
+
 int num_tile_configs();
 const TileConfig& tile_config(int id);
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);

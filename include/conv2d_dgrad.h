@@ -273,6 +273,46 @@ int conv2d_forward_check(const void* x, const void* w, const void* bias, void* z
                          int N, int H, int W, int C, int K, int R, int S,
                          int stride, int pad, int act);
 
+/*
+ * Two dgrad steps of a bottleneck fused into one kernel: the persistent
+ * kernel fusion of the Bolt paper notes (KuangjuX/Paper-reading #28,
+ * "Persistent kernel (GEMM/Conv) fusion"), with threadblock residence (a
+ * workgroup owns all Cm intermediate channels of its 128 pixels) and the
+ * intermediate tile held in shared memory (LDS) between the two GEMMs:
+ *
+ *   t[n,h,w,c]   = fp16( g(z[n,h,w,c]) * sum over r,s,k of
+ *                        dy[n, h + pad - r, w + pad - s, k] * w1[k,r,s,c] )
+ *   dx[n,h,w,ci] = fp16( sum over c of t[n,h,w,c] * w2[c,ci] )
+ *
+ * with the taps of the first sum limited to 0 <= h + pad - r < P and
+ * 0 <= w + pad - s < Q. The first step is conv2d_dgrad_nhwc at stride 1
+ * with its epilogue (g = 1, relu' or hardswish' of z, CONV2D_DGRAD_EPI_*);
+ * the second is the dgrad of the 1x1 stride-1 convolution that made the
+ * first convolution's input. Both accumulate in fp32; t is rounded once to
+ * fp16, as the two separate calls would store it, and is never written to
+ * memory.
+ *
+ * Arguments:
+ *   dy [N][P][Q][K]   fp16, P = H + 2*pad - R + 1, Q = W + 2*pad - S + 1
+ *   w1 [K][R][S][Cm]  fp16 filter of the RxS convolution (Cm -> K channels)
+ *   z  [N][H][W][Cm]  fp16 saved pre-activation (ignored for EPI_NONE)
+ *   w2 [Cm][1][1][C]  fp16 filter of the 1x1 convolution (C -> Cm channels)
+ *   dx [N][H][W][C]   fp16 output, fully written, never read
+ * Limits: those of conv2d_dgrad_nhwc at stride 1 for the first step, plus
+ * Cm <= 128 (the resident tile) and C a multiple of 8 with N*H*W*C and Cm*C
+ * below 2^30. dx must not overlap any input. Pointers 16-byte aligned. The
+ * caller owns all buffers; no workspace; asynchronous on `stream`. Returns
+ * a CONV2D_DGRAD_* status; on error nothing is launched.
+ */
+int conv2d_dgrad_chain_nhwc(const void* dy, const void* w1, const void* z, const void* w2, void* dx,
+                            int N, int H, int W, int Cm, int K, int R, int S, int pad, int C,
+                            int epilogue, void* stream);
+
+/* Validation alone (no HIP call) for conv2d_dgrad_chain_nhwc. */
+int conv2d_dgrad_chain_check(const void* dy, const void* w1, const void* z, const void* w2, const void* dx,
+                             int N, int H, int W, int Cm, int K, int R, int S, int pad, int C,
+                             int epilogue);
+
 /* Thread-local text of the last error ("" if none). */
 const char* conv2d_dgrad_last_error(void);
 

@@ -61,6 +61,8 @@ def _bind(lib):
     lib.oracle_wgrad_rows.restype = i
     lib.oracle_forward_rows.argtypes = [u16p, u16p, u16p] + [i] * 10 + [i64p, ctypes.c_int64, f64p, f64p, i]
     lib.oracle_forward_rows.restype = i
+    lib.oracle_chain_rows.argtypes = [u16p, u16p, u16p, u16p] + [i] * 10 + [i64p, ctypes.c_int64, f64p, f64p, i]
+    lib.oracle_chain_rows.restype = i
     lib.oracle_hardswish.argtypes = [ctypes.c_double]
     lib.oracle_hardswish.restype = ctypes.c_double
     lib.oracle_round_to_half.argtypes = [f64p, u16p, ctypes.c_int64]
@@ -194,6 +196,49 @@ def forward(x, w, bias, stride, pad, act=1, rows=None, threads=0, lib=None):
     if rows is None:
         return z.reshape(N, P, Q, K), y.reshape(N, P, Q, K)
     return z, y
+
+
+def chain(dy, w1, z, w2, H, W, pad, epilogue=EPI_NONE, rows=None, with_abs=False, threads=0, lib=None):
+    """fp64 chain of two dgrad steps: t = fp16(dgrad(dy, w1; stride 1, pad) * g(z)),
+    then dx = t @ w2 over the Cm channels.
+
+    dy [N,P,Q,K], w1 [K,R,S,Cm], z [N,H,W,Cm] (for an epilogue), w2 [Cm,1,1,C]
+    or [Cm,C], all float16. Returns dx [N,H,W,C] float64 (unrounded), or
+    [len(rows), C] for linear pixel indices ``rows``; with ``with_abs`` also
+    sum_c |t||w2| of the same shape.
+    """
+    lib = lib or load()
+    N, P, Q, K = dy.shape
+    K2, R, S, Cm = w1.shape
+    w2m = np.asarray(w2).reshape(w2.shape[0], -1)
+    if K2 != K or w2m.shape[0] != Cm:
+        raise ValueError("dy, w1 and w2 disagree on K or Cm")
+    C = w2m.shape[1]
+    if (lib.oracle_out_extent(H, R, 1, pad), lib.oracle_out_extent(W, S, 1, pad)) != (P, Q):
+        raise ValueError("dy spatial shape does not match H, W, R, S, pad at stride 1")
+    dyk, dyp = _u16(dy)
+    w1k, w1p = _u16(w1)
+    w2k, w2p = _u16(np.ascontiguousarray(w2m))
+    zk = zp = None
+    if epilogue != EPI_NONE:
+        if z is None or tuple(z.shape) != (N, H, W, Cm):
+            raise ValueError("epilogue needs z of shape [N,H,W,Cm]")
+        zk, zp = _u16(z)
+    rr = np.arange(N * H * W, dtype=np.int64) if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.empty((len(rr), C), dtype=np.float64)
+    mag = np.empty((len(rr), C), dtype=np.float64) if with_abs else None
+    f64p = ctypes.POINTER(ctypes.c_double)
+    rc = lib.oracle_chain_rows(dyp, w1p, zp, w2p, N, H, W, Cm, K, R, S, pad, C, epilogue,
+                               rr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(rr),
+                               out.ctypes.data_as(f64p), mag.ctypes.data_as(f64p) if with_abs else None,
+                               int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_chain failed with code {rc}")
+    del dyk, w1k, w2k, zk
+    if rows is None:
+        out = out.reshape(N, H, W, C)
+        mag = mag.reshape(N, H, W, C) if with_abs else None
+    return (out, mag) if with_abs else out
 
 
 def hardswish(zv: float, lib=None) -> float:

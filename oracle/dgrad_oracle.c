@@ -460,6 +460,72 @@ int oracle_forward_rows(const uint16_t* x, const uint16_t* wt, const uint16_t* b
     return failed ? 2 : 0;
 }
 
+/*
+ * Two dgrad steps of a bottleneck, one after the other: the chain that the
+ * persistent kernel fusion of the Bolt paper notes (KuangjuX/Paper-reading
+ * #28, "Persistent kernel (GEMM/Conv) fusion") runs as one kernel. Its
+ * arithmetic is that of the two separate calls:
+ *
+ *   t[c]   = fp16_RNE( dgrad(dy, w1; stride 1, pad)[pixel, c] * g(z[pixel, c]) )
+ *   dx[ci] = sum over c < Cm of t[c] * w2[c][ci]        (fp64, unrounded)
+ *
+ * w1 [K][R][S][Cm] is the RxS filter, w2 [Cm][C] the 1x1 filter of the
+ * convolution in front of it (its dgrad is a plain product over channels).
+ * t is rounded once to fp16 because the unfused pair stores it in fp16
+ * between the calls (a reading: the notes fuse without saying what the
+ * intermediate precision is). mag (may be NULL): sum over c of
+ * |t[c]| * |w2[c][ci]|, the scale of the rounding error of dx.
+ *
+ * rows: linear pixel indices (n*H + h)*W + w; out, mag: [nrows][C].
+ * Returns 0 on success, 1 on invalid arguments, 2 on allocation failure.
+ */
+int oracle_chain_rows(const uint16_t* dy, const uint16_t* w1, const uint16_t* z, const uint16_t* w2,
+                      int N, int H, int W, int Cm, int K, int R, int S, int pad, int C, int epi,
+                      const int64_t* rows, int64_t nrows, double* out, double* mag, int nthreads)
+{
+    if (C < 1 || Cm < 1 || w2 == NULL || nrows < 0 || (nrows > 0 && out == NULL))
+        return 1;
+    double* t = (double*)malloc(sizeof(double) * (size_t)(nrows * Cm + 1));
+    double* w2d = (double*)malloc(sizeof(double) * (size_t)Cm * (size_t)C);
+    if (!t || !w2d) {
+        free(t);
+        free(w2d);
+        return 2;
+    }
+    const int rc = oracle_dgrad_rows(dy, w1, z, N, H, W, Cm, K, R, S, 1, pad, epi, rows, nrows, t, nthreads);
+    if (rc != 0) {
+        free(t);
+        free(w2d);
+        return rc;
+    }
+    for (int64_t i = 0; i < (int64_t)Cm * C; ++i)
+        w2d[i] = oracle_half_to_double(w2[i]);
+    if (nthreads < 1)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 8)
+    for (int64_t it = 0; it < nrows; ++it) {
+        double* o = out + it * (int64_t)C;
+        double* m = mag ? mag + it * (int64_t)C : NULL;
+        for (int ci = 0; ci < C; ++ci) {
+            o[ci] = 0.0;
+            if (m)
+                m[ci] = 0.0;
+        }
+        for (int c = 0; c < Cm; ++c) {
+            const double tc = oracle_half_to_double(oracle_double_to_half_rne(t[it * (int64_t)Cm + c]));
+            const double* wrow = w2d + (int64_t)c * C;
+            for (int ci = 0; ci < C; ++ci) {
+                o[ci] += tc * wrow[ci];
+                if (m)
+                    m[ci] += fabs(tc) * fabs(wrow[ci]);
+            }
+        }
+    }
+    free(t);
+    free(w2d);
+    return 0;
+}
+
 /* RNE fp16 encoding of an fp64 array (bit-exact comparisons). */
 void oracle_round_to_half(const double* in, uint16_t* out, int64_t n)
 {

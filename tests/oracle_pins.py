@@ -542,6 +542,106 @@ def check_forward_adjoint_dgrad(lib):
         assert np.isclose(lhs, rhs, rtol=1e-11, atol=1e-11)
 
 
+# ------------------------------------------------- chain of two dgrad steps
+
+
+def _grad_factor(epi, z):
+    """relu'(z) = [z > 0]; hardswish'(z) = 0 below -3, z/3 + 1/2 on [-3, 3],
+    1 above 3 (the textbook derivative of z * min(max(z + 3, 0), 6) / 6)."""
+    z = np.asarray(z, dtype=np.float64)
+    if epi == oracle.EPI_NONE:
+        return np.ones_like(z)
+    if epi == oracle.EPI_DRELU:
+        return (z > 0).astype(np.float64)
+    return np.where(z < -3, 0.0, np.where(z > 3, 1.0, z / 3 + 0.5))
+
+
+def check_chain_hand_examples(lib):
+    """One pixel, 1x1 filters, worked by hand.
+
+    dy = 2, w1 = 3, w2 = [0.5, -1]: the first step gives 6; relu'(1) = 1
+    keeps it, so dx = 6 * [0.5, -1] = [3, -6]. With hardswish' at z = 0 the
+    factor is 1/2: t = 3 and dx = [1.5, -3], and sum |t||w2| = [1.5, 3].
+    Rounding of t: K = 2, dy = [1, 1], w1 = [1, 2^-11] gives 1 + 2^-11, the
+    midpoint between the fp16 neighbours 1 and 1 + 2^-10; ties to even give
+    t = 1, so with w2 = 1 the chain yields exactly 1 (not 1 + 2^-11).
+    """
+    one = lambda v, shape: f16(np.asarray(v, dtype=np.float64).reshape(shape))
+    dy, w1 = one([2.0], (1, 1, 1, 1)), one([3.0], (1, 1, 1, 1))
+    w2 = one([0.5, -1.0], (1, 1, 1, 2))
+    got = oracle.chain(dy, w1, one([1.0], (1, 1, 1, 1)), w2, 1, 1, 0, oracle.EPI_DRELU, lib=lib)
+    assert np.array_equal(got.reshape(-1), [3.0, -6.0])
+    got, mag = oracle.chain(dy, w1, one([0.0], (1, 1, 1, 1)), w2, 1, 1, 0, oracle.EPI_DHARDSWISH,
+                            with_abs=True, lib=lib)
+    assert np.array_equal(got.reshape(-1), [1.5, -3.0]) and np.array_equal(mag.reshape(-1), [1.5, 3.0])
+    got = oracle.chain(one([1.0, 1.0], (1, 1, 1, 2)), one([1.0, 2.0 ** -11], (2, 1, 1, 1)), None,
+                       one([1.0], (1, 1, 1, 1)), 1, 1, 0, lib=lib)
+    assert got.reshape(-1)[0] == 1.0
+
+
+CHAIN_CASES = [(2, 7, 6, 16, 8, 24, 3, 3, 1), (1, 5, 9, 8, 16, 8, 3, 3, 1), (1, 6, 6, 8, 8, 16, 1, 1, 0),
+               (2, 4, 5, 24, 8, 16, 3, 3, 0), (1, 8, 7, 8, 24, 32, 5, 3, 2)]
+
+
+def _chain_inputs(rng, N, H, W, Cm, K, C, R, S, pad):
+    P, Q = _ext(H, R, 1, pad), _ext(W, S, 1, pad)
+    dy = f16(rng.standard_normal((N, P, Q, K)))
+    w1 = f16(rng.standard_normal((K, R, S, Cm)) / np.sqrt(K * R * S))
+    z = f16(rng.standard_normal((N, H, W, Cm)) * 2.5)
+    w2 = f16(rng.standard_normal((Cm, 1, 1, C)) / np.sqrt(Cm))
+    return dy, w1, z, w2
+
+
+def check_chain_torch(lib):
+    """Cross-check with PyTorch's CPU fp64 input gradients: the RxS step,
+    the textbook derivative factor, numpy's RNE cast of t to fp16, then the
+    1x1 step, for every epilogue kind."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(61))
+    for (N, H, W, Cm, K, C, R, S, pad) in CHAIN_CASES:
+        dy, w1, z, w2 = _chain_inputs(rng, N, H, W, Cm, K, C, R, S, pad)
+        a = torch.nn.grad.conv2d_input(
+            (N, Cm, H, W), torch.from_numpy(w1.astype(np.float64)).permute(0, 3, 1, 2).contiguous(),
+            torch.from_numpy(dy.astype(np.float64)).permute(0, 3, 1, 2).contiguous(),
+            stride=1, padding=pad).permute(0, 2, 3, 1).numpy()
+        for epi in (oracle.EPI_NONE, oracle.EPI_DRELU, oracle.EPI_DHARDSWISH):
+            t = (a * _grad_factor(epi, z)).astype(np.float16).astype(np.float64)
+            ref = torch.nn.grad.conv2d_input(
+                (N, C, H, W), torch.from_numpy(w2.astype(np.float64)).permute(0, 3, 1, 2).contiguous(),
+                torch.from_numpy(t).permute(0, 3, 1, 2).contiguous(), stride=1, padding=0).permute(0, 2, 3, 1).numpy()
+            got = oracle.chain(dy, w1, z, w2, H, W, pad, epi, lib=lib)
+            assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_chain_identity_second_step(lib):
+    """With w2 the identity (C = Cm) the chain is the first step rounded to
+    fp16, i.e. the separately pinned dgrad with its epilogue."""
+    rng = np.random.Generator(np.random.PCG64(62))
+    for (N, H, W, Cm, K, _, R, S, pad) in CHAIN_CASES[:3]:
+        dy, w1, z, _ = _chain_inputs(rng, N, H, W, Cm, K, 8, R, S, pad)
+        eye = f16(np.eye(Cm).reshape(Cm, 1, 1, Cm))
+        for epi in (oracle.EPI_DRELU, oracle.EPI_DHARDSWISH):
+            got = oracle.chain(dy, w1, z, eye, H, W, pad, epi, lib=lib)
+            ref = oracle.dgrad(dy, w1, H, W, 1, pad, epi, z, lib=lib).astype(np.float16).astype(np.float64)
+            assert np.array_equal(got, ref)
+
+
+def check_chain_rows_and_abs(lib):
+    """Sampled pixels equal the full result's rows; the magnitude sum bounds
+    |dx| and equals it when every t and w2 is non-negative."""
+    rng = np.random.Generator(np.random.PCG64(63))
+    N, H, W, Cm, K, C, R, S, pad = CHAIN_CASES[0]
+    dy, w1, z, w2 = _chain_inputs(rng, N, H, W, Cm, K, C, R, S, pad)
+    full, mag = oracle.chain(dy, w1, z, w2, H, W, pad, oracle.EPI_DHARDSWISH, with_abs=True, lib=lib)
+    rows = np.array([0, 5, N * H * W - 1, 17], dtype=np.int64)
+    part, pmag = oracle.chain(dy, w1, z, w2, H, W, pad, oracle.EPI_DHARDSWISH, rows=rows, with_abs=True, lib=lib)
+    assert np.array_equal(part, full.reshape(-1, C)[rows]) and np.array_equal(pmag, mag.reshape(-1, C)[rows])
+    assert np.all(mag >= np.abs(full))
+    got, mag = oracle.chain(f16(np.abs(dy)), f16(np.abs(w1)), None, f16(np.abs(w2)), H, W, pad,
+                            with_abs=True, lib=lib)
+    assert np.array_equal(got, mag)
+
+
 ALL_CHECKS = [
     check_fp16_decode, check_fp16_rne_encode, check_out_extent, check_hand_examples,
     check_scatter_bruteforce, check_adjoint_identity, check_adjoint_unit_vectors,
@@ -551,6 +651,7 @@ ALL_CHECKS = [
     check_wgrad_unit_vectors, check_wgrad_matmul_special_cases, check_wgrad_torch_conv2d_weight,
     check_wgrad_rows_and_abs,
     check_forward_hand_examples, check_forward_vs_slicing, check_forward_torch, check_forward_adjoint_dgrad,
+    check_chain_hand_examples, check_chain_torch, check_chain_identity_second_step, check_chain_rows_and_abs,
 ]
 
 

@@ -158,6 +158,45 @@ def test_forward_configs_and_bad_calls():
     assert e.value.code == cb.INVALID_ARGUMENT
 
 
+W2 = 0x60000000   # second filter of the chain
+CG = dict(N=2, H=8, W=8, Cm=64, K=32, R=3, S=3, pad=1, C=128)
+
+
+def ccheck(dy=DY, w1=WP, z=Z, w2=W2, dx=DX, epi=cb.EPI_DHARDSWISH, **kw):
+    a = dict(CG)
+    a.update(kw)
+    return cb.conv2d_dgrad_chain_check(dy, w1, z, w2, dx, a["N"], a["H"], a["W"], a["Cm"], a["K"], a["R"], a["S"],
+                                       a["pad"], a["C"], epi)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, cb.OK), ({"epi": cb.EPI_NONE, "z": 0}, cb.OK), ({"Cm": 128}, cb.OK), ({"Cm": 8, "C": 8}, cb.OK),
+    ({"epi": cb.EPI_DRELU, "z": 0}, cb.INVALID_ARGUMENT),          # z missing
+    ({"epi": 3}, cb.INVALID_ARGUMENT),
+    ({"N": 0}, cb.INVALID_ARGUMENT), ({"C": 0}, cb.INVALID_ARGUMENT), ({"pad": -1}, cb.INVALID_ARGUMENT),
+    ({"H": 1, "R": 5, "pad": 0}, cb.INVALID_ARGUMENT),             # P < 1
+    ({"dy": 0}, cb.INVALID_ARGUMENT), ({"w1": 0}, cb.INVALID_ARGUMENT), ({"w2": 0}, cb.INVALID_ARGUMENT),
+    ({"dx": 0}, cb.INVALID_ARGUMENT),
+    ({"w2": W2 + 8}, cb.INVALID_ARGUMENT),                          # misaligned
+    ({"dx": DY + 16}, cb.INVALID_ARGUMENT),                         # dx overlaps dy
+    ({"dx": W2 + 64}, cb.INVALID_ARGUMENT),                         # dx overlaps w2
+    ({"dx": Z + 16}, cb.INVALID_ARGUMENT),                          # dx overlaps z
+    ({"Cm": 136}, cb.UNSUPPORTED),                                  # more than one resident tile of channels
+    ({"Cm": 60}, cb.UNSUPPORTED), ({"C": 12}, cb.UNSUPPORTED), ({"K": 4}, cb.UNSUPPORTED),
+    ({"N": 70000, "H": 64, "W": 64, "C": 8, "Cm": 8, "K": 8}, cb.UNSUPPORTED),   # dx of 2^31 elements
+])
+def test_chain_validation_codes(kw, code):
+    assert ccheck(**kw) == code
+    if code != cb.OK:
+        assert cb.conv2d_dgrad_last_error() != ""
+
+
+def test_chain_bad_call_raises_before_launch():
+    with pytest.raises(cb.DgradError) as e:
+        cb.conv2d_dgrad_chain_nhwc(DY, WP, Z, W2, DX, 2, 8, 8, 200, 32, 3, 3, 1, 128, cb.EPI_DHARDSWISH, stream=0)
+    assert e.value.code == cb.UNSUPPORTED
+
+
 def test_invalid_call_returns_before_any_hip_call():
     # conv2d_dgrad_nhwc with a bad argument fails with the validation code,
     # not a HIP error, on a host without a GPU.

@@ -44,6 +44,10 @@ MUTANTS = {
     "forward_hardswish_clamp": ("if (g > 6.0)", "if (g > 3.0)"),
     "forward_filter_taps_swapped": ("wt + (((int64_t)k * R + r) * S + t) * C", "wt + (((int64_t)k * S + t) * R + r) * C"),
     "forward_output_decode": ("const int p = (int)((pix / Q) % P);", "const int p = (int)((pix / P) % Q);"),
+    "chain_t_unrounded": ("oracle_half_to_double(oracle_double_to_half_rne(t[it * (int64_t)Cm + c]))",
+                          "t[it * (int64_t)Cm + c]"),
+    "chain_w2_transposed": ("o[ci] += tc * wrow[ci];", "o[ci] += tc * w2d[(int64_t)ci * Cm + c];"),
+    "chain_epilogue_dropped": ("1, pad, epi, rows, nrows, t, nthreads", "1, pad, 0, rows, nrows, t, nthreads"),
 }
 
 _CHILD = r"""

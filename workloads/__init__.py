@@ -188,8 +188,87 @@ def one_hot_dy(cfg, n, p, q, k, value=1.0) -> np.ndarray:
     return dy
 
 
+@dataclass(frozen=True)
+class ChainConfig:
+    """Two dgrad steps of a bottleneck: the RxS stride-1 convolution
+    (Cm -> K channels, filter w1 [K][R][S][Cm]) and the 1x1 convolution in
+    front of it (C -> Cm, filter w2 [Cm][1][1][C]), with the activation
+    derivative between them taken from z [N][H][W][Cm]."""
+    name: str
+    N: int
+    H: int
+    W: int
+    Cm: int
+    K: int
+    R: int
+    S: int
+    pad: int
+    C: int
+    epilogue: int = EPI_DHARDSWISH
+    z_std: float = 1.5
+    seed: int = 0
+
+    @property
+    def P(self) -> int:
+        return self.H + 2 * self.pad - self.R + 1
+
+    @property
+    def Q(self) -> int:
+        return self.W + 2 * self.pad - self.S + 1
+
+    def useful_flops(self) -> int:
+        """Multiply-adds of both forward layers, times 2."""
+        return 2 * (self.N * self.P * self.Q * self.K * self.Cm * self.R * self.S
+                    + self.N * self.H * self.W * self.Cm * self.C)
+
+    def algorithmic_bytes(self) -> int:
+        """dy + w1 + z + w2 + dx in fp16, each moved once (t stays on chip)."""
+        b = 2 * (self.N * self.P * self.Q * self.K + self.K * self.R * self.S * self.Cm
+                 + self.Cm * self.C + self.N * self.H * self.W * self.C)
+        if self.epilogue != EPI_NONE:
+            b += 2 * self.N * self.H * self.W * self.Cm
+        return b
+
+
+# ResNet-50 stage-2 bottleneck (56x56, 64 mid channels, 256 block channels):
+# the 3x3 conv2 and the 1x1 conv1 in front of it.
+CHAINS = [
+    ChainConfig(name="r50_stage2_chain_3x3_1x1_n8", N=8, H=56, W=56, Cm=64, K=64, R=3, S=3, pad=1, C=256,
+                seed=2001),
+    ChainConfig(name="r50_stage2_chain_3x3_1x1_n256", N=256, H=56, W=56, Cm=64, K=64, R=3, S=3, pad=1, C=256,
+                seed=2002),
+]
+CHAIN_BY_NAME = {c.name: c for c in CHAINS}
+
+
+def make_chain_inputs(cfg: ChainConfig, seed=None) -> dict:
+    """dy ~ N(0,1), w1 ~ N(0, 1/sqrt(K*R*S)), z ~ N(0, z_std) (if the chain
+    has an activation derivative), w2 ~ N(0, 1/sqrt(Cm)); float16, drawn in
+    that order."""
+    rng = np.random.Generator(np.random.PCG64(cfg.seed if seed is None else seed))
+    dy = _normal16(rng, (cfg.N, cfg.P, cfg.Q, cfg.K), 1.0)
+    w1 = _normal16(rng, (cfg.K, cfg.R, cfg.S, cfg.Cm), 1.0 / math.sqrt(cfg.K * cfg.R * cfg.S))
+    z = _normal16(rng, (cfg.N, cfg.H, cfg.W, cfg.Cm), cfg.z_std) if cfg.epilogue != EPI_NONE else None
+    w2 = _normal16(rng, (cfg.Cm, 1, 1, cfg.C), 1.0 / math.sqrt(cfg.Cm))
+    return {"dy": dy, "w1": w1, "z": z, "w2": w2}
+
+
+def integer_chain_inputs(cfg: ChainConfig, seed=11) -> dict:
+    """dy, w1, w2 in {-1, 0, 1} and z from {-4, -1.5, 0, 1.5, 4} (relu' and
+    hardswish' are then 0, 1/2 or 1): every intermediate sum is exact in fp32
+    and every t exact in fp16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dy = rng.integers(-1, 2, size=(cfg.N, cfg.P, cfg.Q, cfg.K)).astype(np.float16)
+    w1 = rng.integers(-1, 2, size=(cfg.K, cfg.R, cfg.S, cfg.Cm)).astype(np.float16)
+    vals = np.array([-4.0, -1.5, 0.0, 1.5, 4.0])
+    z = vals[rng.integers(0, len(vals), size=(cfg.N, cfg.H, cfg.W, cfg.Cm))].astype(np.float16)
+    w2 = rng.integers(-1, 2, size=(cfg.Cm, 1, 1, cfg.C)).astype(np.float16)
+    return {"dy": dy, "w1": w1, "z": z if cfg.epilogue != EPI_NONE else None, "w2": w2}
+
+
 __all__ = [
     "DgradConfig", "CONFIGS", "CONFIG_BY_NAME", "get_config", "make_inputs",
     "small_config", "integer_inputs", "one_hot_dy",
+    "ChainConfig", "CHAINS", "CHAIN_BY_NAME", "make_chain_inputs", "integer_chain_inputs",
     "EPI_NONE", "EPI_DRELU", "EPI_DHARDSWISH", "EPI_NAMES",
 ]
