@@ -125,7 +125,9 @@ __device__ inline int chain_tile(int b, int tiles)
     return x * q + (x < r ? x : r) + l;
 }
 
-template <int CM, int E>
+// NS1 > 0: stage 1 has exactly NS1 slices (taps x k steps), known at compile
+// time, and runs fully unrolled with a deeper prefetch; 0: any count.
+template <int CM, int E, int NS1>
 __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
 {
     using L = ChainLayout<CM>;
@@ -164,15 +166,20 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
         ld_base[j] = ((n * (uint32_t)a.P + h + (uint32_t)a.pad) * (uint32_t)a.Q + w + (uint32_t)a.pad) * (uint32_t)a.K +
                      (uint32_t)(ld_chunk * 8);
     }
-    u32x4 rdy[2], rw1[W1_LD];
-    auto load1 = [&](int r, int s, int k0) {
+    // Register sets of prefetched stage-1 slices: slice j is loaded into set
+    // j % DEPTH. With a known slice count the walk is unrolled, so the
+    // compiler tracks each set's loads exactly and waits only for the slice
+    // it stores next, DEPTH - 1 slices of loads staying in flight.
+    constexpr int DEPTH = NS1 > 0 ? 3 : 1;
+    u32x4 rdy[DEPTH][2], rw1[DEPTH][W1_LD];
+    auto load1 = [&](u32x4 (&ldy)[2], u32x4 (&lw1)[W1_LD], int r, int s, int k0) {
         const uint32_t tapoff = ((uint32_t)r * (uint32_t)a.Q + (uint32_t)s) * (uint32_t)a.K;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int p = ld_hp[j] - r, q = ld_wp[j] - s;
             const uint32_t bad = (uint32_t)!(((unsigned)p < (unsigned)a.P) & ((unsigned)q < (unsigned)a.Q) &
                                              (k0 + ld_chunk * 8 < a.K));
-            rdy[j] = __builtin_amdgcn_raw_buffer_load_b128(dy_r, oor_if(bad, (ld_base[j] - tapoff + (uint32_t)k0) * 2u), 0, 0);
+            ldy[j] = __builtin_amdgcn_raw_buffer_load_b128(dy_r, oor_if(bad, (ld_base[j] - tapoff + (uint32_t)k0) * 2u), 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < W1_LD; ++j) {
@@ -181,21 +188,21 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
             const int k = k0 + krow, c = cc * 8;
             const uint32_t bad = (uint32_t)((k >= a.K) | (c >= a.Cm));
             const uint32_t off = ((((uint32_t)k * (uint32_t)a.R + (uint32_t)r) * (uint32_t)a.S + (uint32_t)s) * (uint32_t)a.Cm + (uint32_t)c) * 2u;
-            rw1[j] = __builtin_amdgcn_raw_buffer_load_b128(w1_r, oor_if(bad, off), 0, 0);
+            lw1[j] = __builtin_amdgcn_raw_buffer_load_b128(w1_r, oor_if(bad, off), 0, 0);
         }
     };
-    auto store1 = [&](int buf) {
+    auto store1 = [&](const u32x4 (&ldy)[2], const u32x4 (&lw1)[W1_LD], int buf) {
         char* st = lds + buf * L::STAGE1;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row = (tid >> 3) + 64 * j;
-            *(u32x4*)(st + row * 128 + ((ld_chunk ^ row_swizzle(row)) * 16)) = rdy[j];
+            *(u32x4*)(st + row * 128 + ((ld_chunk ^ row_swizzle(row)) * 16)) = ldy[j];
         }
 #pragma unroll
         for (int j = 0; j < W1_LD; ++j) {
             const int i = tid + kThreads * j;
             const int krow = i / (CM / 8), cc = i % (CM / 8);
-            *(u32x4*)(st + L::DY_BYTES + krow * L::W1_ROW + ((cc ^ filt_swizzle<L::W1_ROW>(krow)) * 16)) = rw1[j];
+            *(u32x4*)(st + L::DY_BYTES + krow * L::W1_ROW + ((cc ^ filt_swizzle<L::W1_ROW>(krow)) * 16)) = lw1[j];
         }
     };
 
@@ -242,37 +249,6 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
         }
     };
 
-    const int ksteps = (a.K + 63) / 64;
-    const int ns1 = a.R * a.S * ksteps;
-    {
-        int r = 0, s = 0, k0 = 0;       // cursor of the slice being loaded
-        auto advance = [&]() {
-            k0 += 64;
-            if (k0 >= a.K) {
-                k0 = 0;
-                if (++s == a.S) {
-                    s = 0;
-                    ++r;
-                }
-            }
-        };
-        load1(r, s, k0);
-        advance();
-        store1(0);
-        __syncthreads();
-        for (int it = 0; it < ns1; ++it) {
-            const bool more = it + 1 < ns1;
-            if (more) {
-                load1(r, s, k0);
-                advance();
-            }
-            compute1(it & 1);
-            if (more)
-                store1((it + 1) & 1);
-            __syncthreads();
-        }
-    }
-
     // ================= stage-2 loader (w2 slices of 64 rows x 128 channels)
     u32x4 rw2[2];
     auto load2 = [&](int u) {
@@ -297,16 +273,12 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
     };
     const int nch = (a.C + kBN2 - 1) / kBN2;
     const int ns2 = nch * KS2;
-    load2(0);
-
-    // ================= epilogue 1: t = fp16(D1 * g(z)) into the resident tile
-    {
-        const int px = prow;             // this lane's pixel within the tile
-        const int m = m0 + px;
-        half4_t tv[FN1][4];
+    // The tile's z values (epilogue 1): fp16 in the accumulator layout.
+    u32x2 zr[FN1][4];
+    auto load_z = [&]() {
         if constexpr (E != 0) {
             const __amdgpu_buffer_rsrc_t z_r = chain_rsrc(a.z, a.z_bytes);
-            u32x2 zr[FN1][4];
+            const int m = m0 + prow;
 #pragma unroll
             for (int fn = 0; fn < FN1; ++fn)
 #pragma unroll
@@ -315,6 +287,78 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
                     const uint32_t bad = (uint32_t)((m >= a.M) | (c >= a.Cm));
                     zr[fn][gq] = __builtin_amdgcn_raw_buffer_load_b64(z_r, oor_if(bad, ((uint32_t)m * (uint32_t)a.Cm + (uint32_t)c) * 2u), 0, 0);
                 }
+        }
+    };
+
+    const int ksteps = (a.K + 63) / 64;
+    const int ns1 = a.R * a.S * ksteps;
+    {
+        int r = 0, s = 0, k0 = 0;       // cursor of the slice being loaded
+        auto advance = [&]() {
+            k0 += 64;
+            if (k0 >= a.K) {
+                k0 = 0;
+                if (++s == a.S) {
+                    s = 0;
+                    ++r;
+                }
+            }
+        };
+        if constexpr (NS1 > 0) {
+#pragma unroll
+            for (int j = 0; j < DEPTH && j < NS1; ++j) {
+                load1(rdy[j], rw1[j], r, s, k0);
+                advance();
+            }
+            store1(rdy[0], rw1[0], 0);
+            __syncthreads();
+            // slice it: refill set it % DEPTH (its slice is in LDS) with slice
+            // it + DEPTH, compute slice it, store slice it + 1 into the other buffer
+#pragma unroll
+            for (int it = 0; it < NS1; ++it) {
+                if (it + DEPTH < NS1) {
+                    load1(rdy[it % DEPTH], rw1[it % DEPTH], r, s, k0);
+                    advance();
+                }
+                if (it == (NS1 > DEPTH ? NS1 - DEPTH : 0)) {
+                    // the last slice is requested: z and the first w2 slice
+                    // take the registers its sets free
+                    load_z();
+                    load2(0);
+                }
+                compute1(it & 1);
+                if (it + 1 < NS1)
+                    store1(rdy[(it + 1) % DEPTH], rw1[(it + 1) % DEPTH], (it + 1) & 1);
+                __syncthreads();
+            }
+        } else {
+            load1(rdy[0], rw1[0], r, s, k0);
+            advance();
+            store1(rdy[0], rw1[0], 0);
+            __syncthreads();
+            for (int it = 0; it < ns1; ++it) {
+                const bool more = it + 1 < ns1;
+                if (more) {
+                    load1(rdy[0], rw1[0], r, s, k0);
+                    advance();
+                }
+                compute1(it & 1);
+                if (more)
+                    store1(rdy[0], rw1[0], (it + 1) & 1);
+                __syncthreads();
+            }
+            load2(0);
+        }
+    }
+
+
+    // ================= epilogue 1: t = fp16(D1 * g(z)) into the resident tile
+    {
+        const int px = prow;             // this lane's pixel within the tile
+        half4_t tv[FN1][4];
+        if constexpr (E != 0) {
+            if constexpr (NS1 == 0)
+                load_z();
 #pragma unroll
             for (int fn = 0; fn < FN1; ++fn)
 #pragma unroll
@@ -412,34 +456,46 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
     }
 }
 
-template <int CM, int E>
+template <int CM, int E, int NS1>
 hipError_t chain_launch_t(const ChainArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((chain_igemm<CM, E>), dim3(a.tiles), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((chain_igemm<CM, E, NS1>), dim3(a.tiles), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int CM, int E>
+template <int CM, int E, int NS1>
 int chain_private_t()
 {
     hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(chain_igemm<CM, E>)) != hipSuccess) {
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(chain_igemm<CM, E, NS1>)) != hipSuccess) {
         (void)hipGetLastError();
         return -1;
     }
     return (int)attr.localSizeBytes;
 }
 
+// Stage-1 slice counts with an unrolled kernel: 3x3 taps at K <= 64.
+constexpr int kChainUnrolledSlices = 9;
+
 using ChainLaunchFn = hipError_t (*)(const ChainArgs&, hipStream_t);
-// [CM == 128][epilogue]
-const ChainLaunchFn kChainLaunch[2][3] = {
-    {&chain_launch_t<64, 0>, &chain_launch_t<64, 1>, &chain_launch_t<64, 2>},
-    {&chain_launch_t<128, 0>, &chain_launch_t<128, 1>, &chain_launch_t<128, 2>},
+// [unrolled][CM == 128][epilogue]
+const ChainLaunchFn kChainLaunch[2][2][3] = {
+    {{&chain_launch_t<64, 0, 0>, &chain_launch_t<64, 1, 0>, &chain_launch_t<64, 2, 0>},
+     {&chain_launch_t<128, 0, 0>, &chain_launch_t<128, 1, 0>, &chain_launch_t<128, 2, 0>}},
+    {{&chain_launch_t<64, 0, 9>, &chain_launch_t<64, 1, 9>, &chain_launch_t<64, 2, 9>},
+     {&chain_launch_t<128, 0, 9>, &chain_launch_t<128, 1, 9>, &chain_launch_t<128, 2, 9>}},
 };
-int (*const kChainPrivate[2][3])() = {
-    {&chain_private_t<64, 0>, &chain_private_t<64, 1>, &chain_private_t<64, 2>},
-    {&chain_private_t<128, 0>, &chain_private_t<128, 1>, &chain_private_t<128, 2>},
+int (*const kChainPrivate[2][2][3])() = {
+    {{&chain_private_t<64, 0, 0>, &chain_private_t<64, 1, 0>, &chain_private_t<64, 2, 0>},
+     {&chain_private_t<128, 0, 0>, &chain_private_t<128, 1, 0>, &chain_private_t<128, 2, 0>}},
+    {{&chain_private_t<64, 0, 9>, &chain_private_t<64, 1, 9>, &chain_private_t<64, 2, 9>},
+     {&chain_private_t<128, 0, 9>, &chain_private_t<128, 1, 9>, &chain_private_t<128, 2, 9>}},
 };
+
+inline int chain_unrolled(const ChainArgs& a)
+{
+    return a.R * a.S * ((a.K + 63) / 64) == kChainUnrolledSlices ? 1 : 0;
+}
 
 }  // namespace
 
@@ -447,14 +503,16 @@ hipError_t launch_chain(const ChainArgs& a, hipStream_t stream)
 {
     if (a.Cm < 1 || a.Cm > 128 || a.epi < 0 || a.epi > 2)
         return hipErrorInvalidValue;
-    return kChainLaunch[a.Cm > 64][a.epi](a, stream);
+    return kChainLaunch[chain_unrolled(a)][a.Cm > 64][a.epi](a, stream);
 }
 
 int chain_private_bytes(int Cm, int epi)
 {
     if (Cm < 1 || Cm > 128 || epi < 0 || epi > 2)
         return -1;
-    return kChainPrivate[Cm > 64][epi]();
+    const int b = kChainPrivate[0][Cm > 64][epi]();
+    const int u = kChainPrivate[1][Cm > 64][epi]();
+    return b < 0 || u < 0 ? -1 : (b > u ? b : u);
 }
 
 int chain_lds_bytes(int Cm)
