@@ -268,3 +268,30 @@ def test_maximum_sizes_bit_exact(name, shape):
     _bits_equal(gpu.reshape(-1, cfg.C)[rows], ref16)
     if cfg.stride == 2 and cfg.R == 1:    # the three zero lattices, everywhere
         assert not np.any(gpu[:, 1::2, :, :]) and not np.any(gpu[:, :, 1::2, :])
+
+
+# ResNet-50 dgrad layers at batch 256 beyond the measured suite (dx channels C,
+# dy channels K): the stage-2/3/4 3x3 convolutions, the stage-4 strided 3x3
+# and a 1x1 expansion, each with one of the epilogues.
+RESNET50_N256 = [
+    ("stage2_3x3", (256, 56, 56, 64, 64, 3, 3, 1, 1), EPI_DHARDSWISH),
+    ("stage2_3x3_plain", (256, 56, 56, 64, 64, 3, 3, 1, 1), EPI_NONE),
+    ("stage3_3x3", (256, 28, 28, 128, 128, 3, 3, 1, 1), EPI_DRELU),
+    ("stage4_3x3", (256, 14, 14, 256, 256, 3, 3, 1, 1), EPI_NONE),
+    ("stage4_3x3_s2", (256, 28, 28, 256, 256, 3, 3, 2, 1), EPI_DHARDSWISH),
+    ("stage2_1x1_expand", (256, 56, 56, 64, 256, 1, 1, 1, 0), EPI_DRELU),
+]
+
+
+@pytest.mark.parametrize("name,shape,epi", RESNET50_N256, ids=[n for n, _, _ in RESNET50_N256])
+def test_resnet50_batch256_layers(name, shape, epi):
+    """Full-size layers in the table-selected configuration: a seeded pixel
+    sample plus the corner and edge pixels of the first and last images
+    against the oracle, and no unwritten element anywhere."""
+    cfg = small_config(*shape, epilogue=epi, seed=17)
+    inp = make_inputs(cfg)
+    note(f"resnet50 batch-256 layer {name} {shape} epilogue {epi}")
+    gpu = run(cfg, inp)
+    assert not np.isnan(gpu).any()
+    rows = sample_rows(cfg, 1500, seed=23)
+    assert_close(gpu.reshape(-1, cfg.C)[rows], ref_rows(cfg, inp, rows), name)
