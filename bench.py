@@ -341,10 +341,9 @@ def main():
     # hardswish', then the 1x1 dgrad, fused in one kernel, against the same two
     # steps as two calls of this library (t stored in fp16 between them); not
     # part of `value`
-    chain = None
-    if args.chain_reps > 0 and not args.only:
+    def chain_block(name):
         from workloads import CHAIN_BY_NAME, make_chain_inputs
-        ccfg = CHAIN_BY_NAME["r50_stage2_chain_3x3_1x1_n256"]
+        ccfg = CHAIN_BY_NAME[name]
         ci = {k: (None if v is None else torch.from_numpy(v).to(dev)) for k, v in make_chain_inputs(ccfg).items()}
         cdx = torch.empty((ccfg.N, ccfg.H, ccfg.W, ccfg.C), dtype=torch.float16, device=dev)
         ct = torch.empty((ccfg.N, ccfg.H, ccfg.W, ccfg.Cm), dtype=torch.float16, device=dev)
@@ -383,9 +382,10 @@ def main():
         else:
             rl = {"bound": "hbm", "achieved": nbytes / (f_avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
         rl["frac"] = rl["achieved"] / rl["peak"]
-        chain = {"note": "dx = dgrad_1x1(fp16(dgrad_3x3(dy, w1) * hardswish'(z)), w2), ResNet-50 stage-2 bottleneck "
-                         "(3x3 64->64 and 1x1 256->64 convolutions) at N=256, seeded synthetic; fused = one kernel "
-                         "with the intermediate tile in LDS, pair = two dgrad calls with t in HBM",
+        chain = {"note": f"dx = dgrad_1x1(fp16(dgrad_3x3(dy, w1) * hardswish'(z)), w2), ResNet-50 bottleneck "
+                         f"(3x3 {ccfg.Cm}->{ccfg.K} and 1x1 {ccfg.C}->{ccfg.Cm} convolutions, {ccfg.H}x{ccfg.W}) at "
+                         f"N={ccfg.N}, seeded synthetic; fused = one kernel with the intermediate tile in LDS, "
+                         "pair = two dgrad calls with t in HBM",
                  "workload": ccfg.name, "fused_us": f_avg * 1e3, "fused_min_us": f_min * 1e3,
                  "pair_us": p_avg * 1e3, "pair_min_us": p_min * 1e3, "speedup": p_avg / f_avg,
                  "tflops": fl / (f_avg * 1e-3) / 1e12, "alg_mb": nbytes / 1e6,
@@ -393,6 +393,12 @@ def main():
         log(f"[chain] {ccfg.name:34s} fused {f_avg*1e3:9.2f} us  pair {p_avg*1e3:9.2f} us  "
             f"{chain['tflops']:7.1f} TFLOP/s  {rl['bound']} {rl['frac']:.1%}")
         del ci, cdx, ct, cdx2
+        return chain
+
+    chain = chain3 = None
+    if args.chain_reps > 0 and not args.only:
+        chain = chain_block("r50_stage2_chain_3x3_1x1_n256")
+        chain3 = chain_block("r50_stage3_chain_3x3_1x1_n256")
 
     flops = sum(cfg.useful_flops() for cfg, _ in layers)
     kernel_ms = sum(p["avg_us"] for p in per_layer) / 1e3
@@ -438,6 +444,7 @@ def main():
         "wgrad": wgrad,
         "forward": fwd,
         "chain": chain,
+        "chain_stage3": chain3,
         "device": torch.cuda.get_device_name(dev),
         "build": cb.conv2d_dgrad_build_info(),
     }

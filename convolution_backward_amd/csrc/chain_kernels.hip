@@ -474,27 +474,38 @@ int chain_private_t()
     return (int)attr.localSizeBytes;
 }
 
-// Stage-1 slice counts with an unrolled kernel: 3x3 taps at K <= 64.
-constexpr int kChainUnrolledSlices = 9;
+// Stage-1 slice counts with an unrolled kernel: 3x3 taps at K <= 64 (nine
+// slices) and at 64 < K <= 128 (eighteen).
+constexpr int kChainUnrolled[2] = {9, 18};
 
 using ChainLaunchFn = hipError_t (*)(const ChainArgs&, hipStream_t);
-// [unrolled][CM == 128][epilogue]
-const ChainLaunchFn kChainLaunch[2][2][3] = {
+// [variant: any count, 9 slices, 18 slices][CM == 128][epilogue]
+const ChainLaunchFn kChainLaunch[3][2][3] = {
     {{&chain_launch_t<64, 0, 0>, &chain_launch_t<64, 1, 0>, &chain_launch_t<64, 2, 0>},
      {&chain_launch_t<128, 0, 0>, &chain_launch_t<128, 1, 0>, &chain_launch_t<128, 2, 0>}},
     {{&chain_launch_t<64, 0, 9>, &chain_launch_t<64, 1, 9>, &chain_launch_t<64, 2, 9>},
      {&chain_launch_t<128, 0, 9>, &chain_launch_t<128, 1, 9>, &chain_launch_t<128, 2, 9>}},
+    {{&chain_launch_t<64, 0, 18>, &chain_launch_t<64, 1, 18>, &chain_launch_t<64, 2, 18>},
+     {&chain_launch_t<128, 0, 18>, &chain_launch_t<128, 1, 18>, &chain_launch_t<128, 2, 18>}},
 };
-int (*const kChainPrivate[2][2][3])() = {
+int (*const kChainPrivate[3][2][3])() = {
     {{&chain_private_t<64, 0, 0>, &chain_private_t<64, 1, 0>, &chain_private_t<64, 2, 0>},
      {&chain_private_t<128, 0, 0>, &chain_private_t<128, 1, 0>, &chain_private_t<128, 2, 0>}},
     {{&chain_private_t<64, 0, 9>, &chain_private_t<64, 1, 9>, &chain_private_t<64, 2, 9>},
      {&chain_private_t<128, 0, 9>, &chain_private_t<128, 1, 9>, &chain_private_t<128, 2, 9>}},
+    {{&chain_private_t<64, 0, 18>, &chain_private_t<64, 1, 18>, &chain_private_t<64, 2, 18>},
+     {&chain_private_t<128, 0, 18>, &chain_private_t<128, 1, 18>, &chain_private_t<128, 2, 18>}},
 };
 
-inline int chain_unrolled(const ChainArgs& a)
+// The kernel variant for a problem: 1 + the index of its unrolled slice
+// count, or 0 (any count).
+inline int chain_variant(const ChainArgs& a)
 {
-    return a.R * a.S * ((a.K + 63) / 64) == kChainUnrolledSlices ? 1 : 0;
+    const int ns1 = a.R * a.S * ((a.K + 63) / 64);
+    for (int v = 0; v < 2; ++v)
+        if (ns1 == kChainUnrolled[v])
+            return v + 1;
+    return 0;
 }
 
 }  // namespace
@@ -503,16 +514,21 @@ hipError_t launch_chain(const ChainArgs& a, hipStream_t stream)
 {
     if (a.Cm < 1 || a.Cm > 128 || a.epi < 0 || a.epi > 2)
         return hipErrorInvalidValue;
-    return kChainLaunch[chain_unrolled(a)][a.Cm > 64][a.epi](a, stream);
+    return kChainLaunch[chain_variant(a)][a.Cm > 64][a.epi](a, stream);
 }
 
 int chain_private_bytes(int Cm, int epi)
 {
     if (Cm < 1 || Cm > 128 || epi < 0 || epi > 2)
         return -1;
-    const int b = kChainPrivate[0][Cm > 64][epi]();
-    const int u = kChainPrivate[1][Cm > 64][epi]();
-    return b < 0 || u < 0 ? -1 : (b > u ? b : u);
+    int most = 0;
+    for (int v = 0; v < 3; ++v) {
+        const int b = kChainPrivate[v][Cm > 64][epi]();
+        if (b < 0)
+            return -1;
+        most = b > most ? b : most;
+    }
+    return most;
 }
 
 int chain_lds_bytes(int Cm)

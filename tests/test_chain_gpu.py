@@ -28,7 +28,8 @@ EPIS = (cb.EPI_NONE, cb.EPI_DRELU, cb.EPI_DHARDSWISH)
 
 # (N, H, W, Cm, K, R, S, pad, C): several pixel tiles with a ragged last one,
 # both resident widths (Cm <= 64 and Cm <= 128) with ragged Cm, ragged K and
-# C, 1x1 and non-square filters, and a single pixel.
+# C, 1x1 and non-square filters, and a single pixel; stage-1 walks of nine
+# and eighteen slices (the unrolled variants) and of other lengths.
 SMALL = [
     (2, 14, 13, 64, 64, 3, 3, 1, 256),
     (1, 9, 11, 128, 32, 3, 3, 1, 136),
@@ -38,6 +39,7 @@ SMALL = [
     (2, 6, 8, 120, 72, 3, 3, 0, 200),
     (1, 1, 1, 16, 8, 1, 1, 0, 8),
     (1, 16, 16, 64, 136, 3, 3, 1, 384),
+    (2, 10, 9, 48, 96, 3, 3, 1, 72),
 ]
 
 

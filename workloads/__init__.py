@@ -230,13 +230,16 @@ class ChainConfig:
         return b
 
 
-# ResNet-50 stage-2 bottleneck (56x56, 64 mid channels, 256 block channels):
-# the 3x3 conv2 and the 1x1 conv1 in front of it.
+# ResNet-50 bottlenecks: the 3x3 conv2 and the 1x1 conv1 in front of it, in
+# stage 2 (56x56, 64 mid channels, 256 block channels) and stage 3 (28x28,
+# 128 mid channels, 512 block channels).
 CHAINS = [
     ChainConfig(name="r50_stage2_chain_3x3_1x1_n8", N=8, H=56, W=56, Cm=64, K=64, R=3, S=3, pad=1, C=256,
                 seed=2001),
     ChainConfig(name="r50_stage2_chain_3x3_1x1_n256", N=256, H=56, W=56, Cm=64, K=64, R=3, S=3, pad=1, C=256,
                 seed=2002),
+    ChainConfig(name="r50_stage3_chain_3x3_1x1_n256", N=256, H=28, W=28, Cm=128, K=128, R=3, S=3, pad=1, C=512,
+                seed=2003),
 ]
 CHAIN_BY_NAME = {c.name: c for c in CHAINS}
 
