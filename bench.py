@@ -1,15 +1,22 @@
 #!/usr/bin/env python3
 """Throughput of the conv2d dgrad hot path on one MI355X.
 
-A step is one pass over the measured ResNet-50 dgrad suite: the batch-8
-stage-2 3x3 layer and the batch-256 layers (3x3 stride 2, the 1x1 stride-2
-downsample, the 1x1 stride-1 reduce, and the stage-4 3x3 with the fused
-hardswish' epilogue), each a single call of the C ABI on synthetic seeded
-inputs already resident in HBM. That covers every part of the path: the
-stride-phase plan, zero phases, the MFMA implicit GEMM, the fused epilogue
+A step is one pass over the measured ResNet-50 dgrad suite: the N=1 14x14
+3x3 layer, the batch-8 stage-2 3x3 layer and the batch-256 layers (3x3
+stride 2, the 1x1 stride-2 downsample, the 1x1 stride-1 reduce, and the
+stage-4 3x3 with the fused hardswish' epilogue), each a single call of the C
+ABI (with a caller-owned workspace) on synthetic seeded inputs already
+resident in HBM. That covers every part of the path: the stride-phase plan,
+zero phases, the MFMA implicit GEMM, the stream-K split, the fused epilogue
 and the tile-config table (filled during warm-up).
 
-value = useful FLOPs of the suite (2*N*P*Q*K*C*R*S per layer) / time per step.
+Timing is cold, as the headline: before every layer call a read of a
+512 MiB buffer evicts the layer's operands from L2 and the Infinity Cache
+(a read, so that no dirty lines are left whose write-back would land inside
+the timed kernel), and HIP events on the launch stream bracket the call
+alone. value = useful FLOPs of the suite (2*N*P*Q*K*C*R*S per layer) / the
+mean over the K steps of the summed per-layer times. The warm (back to
+back) and end-to-end (host call + synchronise) timings are reported beside.
 
 Prints one JSON line (see the fields at the end of main()).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-fraction F]
@@ -29,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 from workloads import CONFIGS, EPI_NAMES, make_inputs, make_x  # noqa: E402
 
-SUITE = [1, 2, 3, 4, 5]            # indices into CONFIGS; 0 is the latency-sized parity case
+SUITE = [0, 1, 2, 3, 4, 5]         # indices into CONFIGS
 MFMA_PEAK_TFLOPS = 2500.0          # MI355X dense fp16 matrix-core peak
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 RIDGE = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
@@ -71,14 +78,27 @@ def measured_traffic(kernel_key):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inputs, fraction, suite, seed=99):
     """The oracle, untuned, on a seeded `fraction` of each layer's output
-    pixels; the full-suite time is extrapolated by 1/fraction per layer."""
+    pixels with every host thread, the full-suite time extrapolated by
+    1/fraction per layer; plus one-thread runs of the two small layers."""
     import oracle
     lib = oracle.load()
     threads = oracle.max_threads(lib)
     total_t = 0.0
     rows_done = 0
+    per_layer = []
     for idx in suite:
         cfg = CONFIGS[idx]
         npix = cfg.N * cfg.H * cfg.W
@@ -92,23 +112,41 @@ def cpu_baseline(inputs, fraction, suite, seed=99):
         dt = time.perf_counter() - t0
         total_t += dt * npix / k
         rows_done += k
-        log(f"[cpu] {cfg.name}: {k} of {npix} pixels in {dt:.2f} s")
+        per_layer.append({"layer": cfg.name, "seconds": dt * npix / k,
+                          "gflops": cfg.useful_flops() / (dt * npix / k) / 1e9})
+        log(f"[cpu] {cfg.name}: {k} of {npix} pixels in {dt:.2f} s ({threads} threads)")
+    one_thread = []
+    for idx in (0, 1):
+        if idx not in inputs:
+            continue
+        cfg, inp = CONFIGS[idx], inputs[idx]
+        t0 = time.perf_counter()
+        oracle.dgrad(inp["dy"], inp["w"], cfg.H, cfg.W, cfg.stride, cfg.pad, cfg.epilogue, inp["z"],
+                     threads=1, lib=lib)
+        dt = time.perf_counter() - t0
+        one_thread.append({"layer": cfg.name, "seconds": dt, "gflops": cfg.useful_flops() / dt / 1e9})
+        log(f"[cpu] {cfg.name}: every pixel on 1 thread in {dt:.2f} s")
     flops = sum(CONFIGS[i].useful_flops() for i in suite)
     return {"value": flops / total_t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"seeded {fraction:.0%} of the output pixels of each suite layer "
-                      f"({rows_done} pixel rows, all channels, fp64); full-suite time extrapolated "
-                      f"per layer by pixel count: {total_t:.1f} s per step"}
+                      f"({rows_done} pixel rows, all channels, fp64, {threads} OpenMP threads); full-suite "
+                      f"time extrapolated per layer by pixel count: {total_t:.2f} s per step",
+            "layers": per_layer, "one_thread": one_thread}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100,
+                    help="timed steps; each layer is launched once per step, cold")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-fraction", type=float, default=1.0,
                     help="share of each layer's pixels the oracle computes for cpu_baseline (0 skips it)")
-    ap.add_argument("--cold-reps", type=int, default=10,
-                    help="cold-cache launches per layer, each after a 512 MiB scratch write (0 skips)")
+    ap.add_argument("--warm-steps", type=int, default=50,
+                    help="back-to-back steps timed as the warm figure (0 skips)")
+    ap.add_argument("--e2e-reps", type=int, default=20,
+                    help="host-timed calls per layer, each followed by a stream synchronisation (0 skips)")
     ap.add_argument("--wgrad-reps", type=int, default=10,
                     help="timed wgrad (filter gradient) calls per layer, after the dgrad timing (0 skips)")
     ap.add_argument("--forward-reps", type=int, default=10,
@@ -155,8 +193,10 @@ def main():
             print(f"--only matched no layer of {[CONFIGS[i].name for i in SUITE]}", file=sys.stderr)
             sys.exit(2)
 
-    # ---- inputs, resident in HBM before timing
+    # ---- inputs, resident in HBM before timing; one workspace (zeroed once,
+    # owned by PyTorch's allocator) serves every layer, as the C ABI allows
     host_inputs, layers = {}, []
+    ws_bytes = 0
     for idx in suite:
         cfg = CONFIGS[idx]
         inp = make_inputs(cfg)
@@ -164,12 +204,15 @@ def main():
         d = {k: (None if v is None else torch.from_numpy(v).to(dev)) for k, v in inp.items()}
         d["dx"] = torch.empty((cfg.N, cfg.H, cfg.W, cfg.C), dtype=torch.float16, device=dev)
         layers.append((cfg, d))
+        ws_bytes = max(ws_bytes, cb.conv2d_dgrad_workspace_size(cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
+                                                                cfg.stride, cfg.pad, cfg.epilogue))
+    workspace = cb.workspace(ws_bytes, dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
     def one_layer(cfg, d):
-        cb.conv2d_dgrad_nhwc(d["dy"], d["w"], d["dx"], cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
-                             cfg.stride, cfg.pad, cfg.epilogue, d["z"], stream.cuda_stream)
+        cb.conv2d_dgrad_nhwc_ws(d["dy"], d["w"], d["dx"], cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
+                                cfg.stride, cfg.pad, cfg.epilogue, d["z"], workspace, stream.cuda_stream)
 
     # ---- warm-up (the first call per layer fills the tile-config table)
     for _ in range(args.warmup):
@@ -177,91 +220,113 @@ def main():
             one_layer(cfg, d)
     torch.cuda.synchronize()
 
-    # ---- timed steps: the layers back to back, nothing else on the stream
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        for cfg, d in layers:
-            one_layer(cfg, d)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # ---- per-layer kernel times: the same steps again, each call bracketed
-    # by HIP events on the launch stream (the event packets stay out of the
-    # timed steps above)
+    # ---- timed steps, cold: before each layer call a 512 MiB read evicts L2
+    # (4 MiB per XCD) and the 256 MiB Infinity Cache; the event pair on the
+    # launch stream brackets the layer call alone
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in layers] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for s in range(args.steps):
         for li, (cfg, d) in enumerate(layers):
+            torch.sum(flush, out=flush_out)
             ev[s][li][0].record(stream)
             one_layer(cfg, d)
             ev[s][li][1].record(stream)
     torch.cuda.synchronize()
+    cold_wall = time.perf_counter() - t0
+    step_ms = [sum(ev[s][li][0].elapsed_time(ev[s][li][1]) for li in range(len(layers))) for s in range(args.steps)]
+    ms_per_step = float(np.mean(step_ms))
 
     per_layer = []
     for li, (cfg, d) in enumerate(layers):
-        ms = [ev[s][li][0].elapsed_time(ev[s][li][1]) for s in range(args.steps)]
+        ms = np.array([ev[s][li][0].elapsed_time(ev[s][li][1]) for s in range(args.steps)])
         avg = float(np.mean(ms))
-        cid, _ = cb.conv2d_dgrad_query_config(cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S, cfg.stride,
-                                              cfg.pad, cfg.epilogue)
+        cid, _, split = cb.conv2d_dgrad_query_config(cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S, cfg.stride,
+                                                     cfg.pad, cfg.epilogue, with_workspace=ws_bytes > 0,
+                                                     with_split=True)
         rl = roofline_of(cfg, avg * 1e-3)
         per_layer.append({
-            "layer": cfg.name, "avg_us": avg * 1e3, "min_us": float(np.min(ms)) * 1e3,
+            "layer": cfg.name, "avg_us": avg * 1e3, "median_us": float(np.median(ms)) * 1e3,
+            "min_us": float(np.min(ms)) * 1e3, "launches": int(len(ms)),
             "tflops": cfg.useful_flops() / (avg * 1e-3) / 1e12,
             "mfma_frac": cfg.useful_flops() / (avg * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
             "alg_gbs": cfg.algorithmic_bytes() / (avg * 1e-3) / 1e9,
             "hbm_frac": cfg.algorithmic_bytes() / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bound": rl["bound"], "roofline_frac": rl["frac"],
-            "tile_config": cb.conv2d_dgrad_config_name(cid),
+            "tile_config": cb.conv2d_dgrad_config_name(cid) + ("+sk" if split else ""),
             "useful_gflop": cfg.useful_flops() / 1e9, "alg_mb": cfg.algorithmic_bytes() / 1e6,
         })
-        log(f"[gpu] {cfg.name:34s} {avg*1e3:9.2f} us  {per_layer[-1]['tflops']:7.1f} TFLOP/s  "
+        log(f"[cold] {cfg.name:34s} {avg*1e3:9.2f} us  {per_layer[-1]['tflops']:7.1f} TFLOP/s  "
             f"{per_layer[-1]['alg_gbs']:7.0f} GB/s  {rl['bound']} {rl['frac']:.1%}  [{per_layer[-1]['tile_config']}]")
+    del flush, flush_out
 
-    # ---- cold cache: before each launch a 512 MiB write on the same stream
-    # evicts L2 (4 MiB per XCD) and the 256 MiB Infinity Cache; the event pair
-    # brackets the dgrad launch alone
-    cold = None
-    if args.cold_reps > 0:
-        scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.int32, device=dev)
-        cold_layers = []
+    # ---- warm: the layers back to back (operands partly in the caches, like
+    # the pages' nvprof averages), wall clock over the steps, then per-layer
+    # HIP events in a second pass
+    warm = None
+    if args.warm_steps > 0:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.warm_steps):
+            for cfg, d in layers:
+                one_layer(cfg, d)
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - t0) * 1e3 / args.warm_steps
+        wev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in layers] for _ in range(args.warm_steps)]
+        for s in range(args.warm_steps):
+            for li, (cfg, d) in enumerate(layers):
+                wev[s][li][0].record(stream)
+                one_layer(cfg, d)
+                wev[s][li][1].record(stream)
+        torch.cuda.synchronize()
+        wl = []
+        for li, (cfg, d) in enumerate(layers):
+            ms = [wev[s][li][0].elapsed_time(wev[s][li][1]) for s in range(args.warm_steps)]
+            avg = float(np.mean(ms))
+            wl.append({"layer": cfg.name, "avg_us": avg * 1e3, "min_us": float(np.min(ms)) * 1e3,
+                       "tflops": cfg.useful_flops() / (avg * 1e-3) / 1e12,
+                       "roofline_frac": roofline_of(cfg, avg * 1e-3)["frac"]})
+            log(f"[warm] {cfg.name:34s} {avg*1e3:9.2f} us  {wl[-1]['tflops']:7.1f} TFLOP/s")
+        warm = {"note": "layers back to back, no flush; value = suite FLOPs / wall time per step",
+                "value": sum(cfg.useful_flops() for cfg, _ in layers) / (warm_ms * 1e-3) / 1e12,
+                "unit": "TFLOP/s", "ms_per_step": warm_ms, "layers": wl}
+
+    # ---- end to end: host time of one C-ABI call plus a stream
+    # synchronisation, the tile table already filled (launch overhead included)
+    e2e = None
+    if args.e2e_reps > 0:
+        el = []
         for cfg, d in layers:
             ts = []
-            for r in range(args.cold_reps):
-                scratch.fill_(r)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                one_layer(cfg, d)
-                e1.record(stream)
+            for _ in range(args.e2e_reps):
                 torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e3)
-            med = float(np.median(ts))
-            cold_layers.append({"layer": cfg.name, "median_us": med, "min_us": float(np.min(ts)),
-                                "tflops": cfg.useful_flops() / (med * 1e-6) / 1e12})
-            log(f"[cold] {cfg.name:34s} {med:9.2f} us (median of {args.cold_reps})")
-        del scratch
-        cold_s = sum(c["median_us"] for c in cold_layers) * 1e-6
-        cold = {"note": "each launch after a 512 MiB scratch write (L2 and Infinity Cache evicted); "
-                        "suite value = useful FLOPs / sum of per-layer medians",
-                "value": sum(cfg.useful_flops() for cfg, _ in layers) / cold_s / 1e12, "unit": "TFLOP/s",
-                "layers": cold_layers}
+                t0 = time.perf_counter()
+                one_layer(cfg, d)
+                stream.synchronize()
+                ts.append((time.perf_counter() - t0) * 1e6)
+            el.append({"layer": cfg.name, "median_us": float(np.median(ts)), "min_us": float(np.min(ts))})
+            log(f"[e2e] {cfg.name:34s} {el[-1]['median_us']:9.2f} us (median of {args.e2e_reps})")
+        e2e = {"note": "host wall time of conv2d_dgrad_nhwc_ws + stream synchronise, operands warm", "layers": el}
 
     # ---- wgrad (the filter gradient, a NEXT row of the same layer): each
-    # layer's dy with a seeded x, automatic tile config and split count,
-    # HIP events around each call (its two kernels); not part of `value`
+    # layer's dy with a seeded x, the table's tile config and split count with
+    # a caller-owned workspace, HIP events around each call (its two
+    # kernels); not part of `value`
     wgrad = None
     if args.wgrad_reps > 0:
         wlayers = []
         for cfg, d in layers:
             x = torch.from_numpy(make_x(cfg)).to(dev)
             dw = torch.empty((cfg.K, cfg.R, cfg.S, cfg.C), dtype=torch.float32, device=dev)
+            wws = cb.wgrad_workspace(cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S, cfg.stride, cfg.pad, dev)
 
             def wcall():
-                cb.conv2d_wgrad_nhwc(d["dy"], x, dw, cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
-                                     cfg.stride, cfg.pad, stream.cuda_stream)
+                cb.conv2d_wgrad_nhwc_ws(d["dy"], x, dw, cfg.N, cfg.H, cfg.W, cfg.C, cfg.K, cfg.R, cfg.S,
+                                        cfg.stride, cfg.pad, wws, stream.cuda_stream)
             for _ in range(3):
                 wcall()
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -285,10 +350,11 @@ def main():
                             "tflops": fl / (avg * 1e-3) / 1e12, "alg_mb": nbytes / 1e6, "roofline": rl})
             log(f"[wgrad] {cfg.name:34s} {avg*1e3:9.2f} us  {wlayers[-1]['tflops']:7.1f} TFLOP/s  "
                 f"{rl['bound']} {rl['frac']:.1%}")
-            del x, dw
+            del x, dw, wws
         wsum = sum(w["avg_us"] for w in wlayers) * 1e-6
         wgrad = {"note": "dw[k,r,s,c] = sum dy*x (fp32 out), x = max(N(0,1),0) seeded; split-K GEMM plus an "
-                         "ordered reduction kernel; suite value = useful FLOPs / sum of per-layer means",
+                         "ordered reduction kernel, partial sums in a caller-owned workspace; warm; suite value = "
+                         "useful FLOPs / sum of per-layer means",
                  "value": sum(cfg.useful_flops() for cfg, _ in layers) / wsum / 1e12, "unit": "TFLOP/s",
                  "layers": wlayers}
 
@@ -401,13 +467,14 @@ def main():
         chain3 = chain_block("r50_stage3_chain_3x3_1x1_n256")
 
     flops = sum(cfg.useful_flops() for cfg, _ in layers)
-    kernel_ms = sum(p["avg_us"] for p in per_layer) / 1e3
     value = flops / (ms_per_step * 1e-3) / 1e12
 
     dom = max(range(len(layers)), key=lambda i: per_layer[i]["avg_us"])
     dcfg = layers[dom][0]
     roof = roofline_of(dcfg, per_layer[dom]["avg_us"] * 1e-6)
     roof["kernel"] = f"dgrad_igemm<{per_layer[dom]['tile_config']}> on {dcfg.name}"
+    roof["unit_of_work"] = ("one layer call = one launch; algorithmic bytes dy + w + dx (+ z), each once, "
+                            f"{dcfg.algorithmic_bytes()} B; cold mean of {args.steps} launches")
     roof["traffic"] = measured_traffic(dcfg.name)
 
     cpu = None
@@ -434,13 +501,18 @@ def main():
             "accumulate": "f32",
             "layout": "NHWC fp16 dy/dx/z, KRSC fp16 filter",
             "useful_gflop_per_step": flops / 1e9,
+            "timing": "cold",
         },
         "mfma_frac_of_peak": value / MFMA_PEAK_TFLOPS,
-        "kernel_ms_per_step": kernel_ms,
+        "timing": "cold: each layer call after a 512 MiB read; per-layer HIP events on the launch stream; "
+                  f"{args.steps} launches per layer; wall time of the timed loop {cold_wall:.3f} s "
+                  "(flushes included)",
         "roofline": roof,
         "cpu_baseline": cpu,
         "layers": per_layer,
-        "cold": cold,
+        "warm": warm,
+        "e2e": e2e,
+        "workspace_bytes": ws_bytes,
         "wgrad": wgrad,
         "forward": fwd,
         "chain": chain,

@@ -126,7 +126,8 @@ struct WgradArgs {
     const uint16_t* dy;
     const uint16_t* x;
     float* dw;           // [K][R][S][C] fp32, fully written
-    float* part;         // [splits][tiles][BC*BK] fp32 partial sums in register order
+    float* part;         // [splits][tiles][BC*BK] fp32 partial sums in register order, or NULL
+                         // with splits == 1: the kernel writes dw directly
     uint32_t dy_bytes;
     uint32_t x_bytes;
     int N, H, W, C, K, R, S, P, Q, stride, pad;

@@ -1233,6 +1233,25 @@ __global__ void __launch_bounds__(64 * WC * WK) wgrad_igemm(WgradArgs a)
         compute(i % 3);
     }
 
+    // One split without a partial buffer: the sums are dw itself. A lane holds
+    // channels 8*q + 4*(lane/32) .. +3 of output channel lane % 32 in each
+    // 32x32 block (the mapping wgrad_reduce applies).
+    if (a.part == nullptr) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = c0 + wc * TC + fn * 32 + 8 * q + 4 * (lane >> 5);
+                    const int k = k0 + wk * TK + fm * 32 + (lane & 31);
+                    if (c < C && k < K)   // C % 8 == 0: the 4 channels are all inside or all outside
+                        *(float4_t*)(a.dw + ((size_t)k * (size_t)(a.R * a.S) + (size_t)tap) * (size_t)C + (size_t)c) =
+                            float4_t{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2],
+                                     acc[fn][fm][4 * q + 3]};
+                }
+        return;
+    }
     // partial sums in register order: 16-byte group q of thread tid at float
     // offset (q*NT + tid)*4 of this (split, tile) block
     float* out = a.part + ((size_t)split * (size_t)tiles + (size_t)tile) * (size_t)(BC * BK);

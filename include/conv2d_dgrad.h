@@ -34,10 +34,24 @@
  * Ownership and execution. All tensor pointers are device pointers owned by
  * the caller, who keeps them alive until the enqueued work completes. Calls
  * are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
- * The library allocates no device memory except the stream-K workspace (see
- * conv2d_dgrad_set_streamk); the caller provides none. dx is never
- * read (it may hold anything, NaN included, before the call). dx must not
- * overlap dy, w or z.
+ * The library allocates no device memory, ever. dx is never read (it may hold
+ * anything, NaN included, before the call). dx must not overlap dy, w or z.
+ *
+ * Workspace (the FindEx pattern of the CUDA.jl PR: the caller, not the
+ * library, allocates, so a pool allocator stays in charge of device memory).
+ * The *_ws and *_config entry points take an optional device workspace that
+ * lets a call split its reduction (stream-K for dgrad, split-K for wgrad).
+ * The *_workspace_size queries give the bytes that let every candidate of a
+ * problem split; a smaller workspace only narrows the choice, and without one
+ * (NULL, 0 bytes) every launch runs whole tiles. Layout and contract:
+ *   - at least 65536 bytes, 16-byte aligned, not overlapping any tensor;
+ *   - the first 65536 bytes hold arrival counters: ZERO THEM ONCE before the
+ *     workspace's first use (e.g. torch.zeros or hipMemset). Every call leaves
+ *     them zero again when its work completes, so one workspace serves any
+ *     number of later calls, of any shape and entry point, without clearing;
+ *   - the rest holds fp32 partial sums; its contents between calls are free;
+ *   - calls that share a workspace must be ordered (one stream, or
+ *     synchronised); calls that overlap in time on one workspace race.
  *
  * Tile-config selection. The first call for a new problem key (every shape
  * argument, the epilogue kind and the device) picks a tile configuration:
@@ -56,6 +70,8 @@
 #ifndef CONV2D_DGRAD_H
 #define CONV2D_DGRAD_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -65,7 +81,9 @@ extern "C" {
 #define CONV2D_DGRAD_INVALID_ARGUMENT 1 /* null pointer, dim < 1, stride < 1, pad < 0,
                                            P or Q < 1, unknown epilogue, z missing,
                                            pointer not 16-byte aligned, dx overlapping
-                                           an input, bad config id */
+                                           an input, bad config id, a workspace below
+                                           65536 bytes, misaligned or overlapping a
+                                           tensor, or NULL with a nonzero size */
 #define CONV2D_DGRAD_UNSUPPORTED 2      /* C or K not a multiple of 8, a tensor of
                                            2^30 elements or more, stride > 16 */
 #define CONV2D_DGRAD_HIP_ERROR 3        /* a HIP runtime call or launch failed */
@@ -92,14 +110,37 @@ int conv2d_dgrad_nhwc(const void* dy, const void* w, void* dx,
                       void* stream);
 
 /*
+ * The same with a caller-owned workspace (see "Workspace" above): launches
+ * whose tiles would leave workgroups idle may then split their reduction
+ * (stream-K, conv2d_dgrad_set_streamk). workspace may be NULL (with
+ * workspace_bytes = 0), which is conv2d_dgrad_nhwc. The table keeps separate
+ * choices for calls with and without a workspace.
+ */
+int conv2d_dgrad_nhwc_ws(const void* dy, const void* w, void* dx,
+                         int N, int H, int W, int C, int K, int R, int S,
+                         int stride, int pad, int epilogue, const void* z,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * *bytes = the workspace size that lets every tile configuration of this
+ * problem take its split (the counter area plus the largest partial-sum area
+ * any candidate plans), or 0 when no candidate can split. Host-only; the
+ * figure assumes the current device's CU count and occupancy.
+ */
+int conv2d_dgrad_workspace_size(int N, int H, int W, int C, int K, int R, int S,
+                                int stride, int pad, int epilogue, size_t* bytes);
+
+/*
  * Same computation with an explicit tile configuration (0 <= config_id <
- * conv2d_dgrad_num_configs()), bypassing the table. For tests that check
- * every candidate and for benchmarks that sweep them.
+ * conv2d_dgrad_num_configs()), bypassing the table, and an optional
+ * workspace as for conv2d_dgrad_nhwc_ws. For tests that check every
+ * candidate and for benchmarks that sweep them.
  */
 int conv2d_dgrad_nhwc_config(const void* dy, const void* w, void* dx,
                              int N, int H, int W, int C, int K, int R, int S,
                              int stride, int pad, int epilogue, const void* z,
-                             int config_id, void* stream);
+                             int config_id, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Number of compiled tile configurations, and a readable name for one
  * ("BMxBNxBK/WMxWN"): buf receives at most buflen bytes, NUL-terminated. */
@@ -107,18 +148,29 @@ int conv2d_dgrad_num_configs(void);
 int conv2d_dgrad_config_name(int config_id, char* buf, int buflen);
 
 /*
- * The configuration the table holds for a problem key, without launching:
- * *config_id = the cached choice, or the heuristic's choice when the key is
- * not cached (*cached = 0). Validates like conv2d_dgrad_nhwc. Needs no GPU
- * when the key is not cached.
+ * The configuration the table holds for a problem key (with_workspace: the
+ * entry for calls that bring a workspace), without launching: *config_id =
+ * the cached choice, or the heuristic's choice when the key is not cached
+ * (*cached = 0); *split (if non-NULL) = 1 when the cached choice splits the
+ * reduction. Validates the shape like conv2d_dgrad_nhwc. Needs no GPU when
+ * the key is not cached.
  */
 int conv2d_dgrad_query_config(int N, int H, int W, int C, int K, int R, int S,
-                              int stride, int pad, int epilogue,
-                              int* config_id, int* cached);
+                              int stride, int pad, int epilogue, int with_workspace,
+                              int* config_id, int* cached, int* split);
 
 /* Autotuning on (1, the default unless the environment sets
  * CONV2D_DGRAD_AUTOTUNE=0) or off (0). Returns the previous setting. */
 int conv2d_dgrad_set_autotune(int on);
+
+/*
+ * Fault injection for the profilers' failure path (also set by the
+ * environment variable CONV2D_DGRAD_FAULT_INJECT=1): while on, every candidate
+ * a profiler would time counts as failed before it is launched, so the
+ * problem keeps the shape heuristic's choice ("Get"), which the CUDA.jl PR
+ * names as the fallback of a failed "Find". Returns the previous setting.
+ */
+int conv2d_dgrad_set_fault_inject(int on);
 
 /*
  * Stream-K split of the reduction. A launch's reduction slices (all its GEMM
@@ -130,17 +182,17 @@ int conv2d_dgrad_set_autotune(int on);
  * sum). This is the "parallel split-k" that the "[CUTLASS] Conv2d dgrad" page
  * (apache/tvm PR #10110) names as follow-up work.
  *
- * The partial sums need a workspace in uncached device memory: the library
- * allocates one per device and stream on first use (outside graph capture)
- * and never frees it; a larger one replaces it when needed, and the old one
- * is kept for graphs that captured it. Under capture without a large enough
- * workspace, or when allocation fails, the launch runs whole tiles. Calls on
- * one stream are ordered by the stream; calls on different streams use
- * different workspaces.
+ * The partial sums and arrival counters live in the caller's workspace
+ * (conv2d_dgrad_nhwc_ws, conv2d_dgrad_nhwc_config); a call without one, or
+ * whose workspace is too small for a launch's partial sums, runs that
+ * launch with whole tiles. A share's partial sums are written and read with
+ * system-scope cache policy, so they pass between the XCDs' separate L2
+ * caches without any cache flush. At most 16384 GEMM tiles per launch split.
  *
  *   mode 0: never split.
- *   mode 1: split every eligible launch (no zero phases, at least one GEMM
- *           tile, partial sums within 1 GiB) as finely as the device allows.
+ *   mode 1: split every eligible launch (no zero phases, 1..16384 GEMM
+ *           tiles, partial sums within 1 GiB and within the workspace) as
+ *           finely as the device allows.
  *   mode 2 (default): the profiler times each tile configuration with and
  *           without the split, and the table keeps the faster (table files
  *           mark a split choice with "+sk" after the config name). For an
@@ -210,22 +262,37 @@ int conv2d_dgrad_check(const void* dy, const void* w, void* dx,
  * Shapes, alignment (16 bytes), limits and status codes are those of
  * conv2d_dgrad_nhwc; dw must not overlap dy or x.
  *
- * Accumulation is fp32 throughout: the N*P*Q-long reduction is cut into
- * contiguous ranges whose fp32 partial sums a second kernel adds in a fixed
- * order, so results do not depend on timing. The partial sums live in a
- * library-owned device workspace per device and stream (at most 1 GiB),
- * allocated on first use outside graph capture and never freed. Calls are
- * asynchronous on `stream`.
+ * Accumulation is fp32 throughout. With a workspace (conv2d_wgrad_nhwc_ws),
+ * the N*P*Q-long reduction is cut into contiguous ranges whose fp32 partial
+ * sums (in the workspace after its counter area) a second kernel adds in a
+ * fixed order, so results do not depend on timing. Without one, a single
+ * range per tile writes dw directly: correct, but with only R*S*ceil(C/BC)*
+ * ceil(K/BK) workgroups it leaves most of the chip idle on large layers.
+ * Calls are asynchronous on `stream`.
  */
 int conv2d_wgrad_nhwc(const void* dy, const void* x, void* dw,
                       int N, int H, int W, int C, int K, int R, int S,
                       int stride, int pad, void* stream);
 
-/* The same with an explicit tile configuration (0 .. conv2d_wgrad_num_configs()-1)
- * and reduction split count (0: automatic, about two workgroups per CU). */
+/* The same with a caller-owned workspace (contract as for dgrad above); the
+ * split count is cut to what the workspace holds. */
+int conv2d_wgrad_nhwc_ws(const void* dy, const void* x, void* dw,
+                         int N, int H, int W, int C, int K, int R, int S,
+                         int stride, int pad, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* *bytes = the workspace that holds the largest split any wgrad candidate of
+ * this problem uses (0 when none splits). Host-only. */
+int conv2d_wgrad_workspace_size(int N, int H, int W, int C, int K, int R, int S,
+                                int stride, int pad, size_t* bytes);
+
+/* The same with an explicit tile configuration (0 .. conv2d_wgrad_num_configs()-1),
+ * reduction split count (0: automatic, about two workgroups per CU; cut to
+ * what the workspace holds) and optional workspace. */
 int conv2d_wgrad_nhwc_config(const void* dy, const void* x, void* dw,
                              int N, int H, int W, int C, int K, int R, int S,
-                             int stride, int pad, int config_id, int splits, void* stream);
+                             int stride, int pad, int config_id, int splits,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of compiled wgrad tile configurations. */
 int conv2d_wgrad_num_configs(void);
@@ -307,6 +374,30 @@ int conv2d_forward_check(const void* x, const void* w, const void* bias, void* z
 int conv2d_dgrad_chain_nhwc(const void* dy, const void* w1, const void* z, const void* w2, void* dx,
                             int N, int H, int W, int Cm, int K, int R, int S, int pad, int C,
                             int epilogue, void* stream);
+
+/*
+ * The same with a caller-owned workspace (contract as above). When the
+ * workspace holds the intermediate t (conv2d_dgrad_chain_workspace_size: the
+ * counter area plus N*H*W*Cm fp16), the chain may instead run as two
+ * conv2d_dgrad_nhwc calls with t stored there, if that is faster: the first
+ * such call for a problem times both paths on the caller's buffers and
+ * stream (with autotuning on, outside graph capture; it synchronises the
+ * stream once) and caches the faster per problem and device. Both paths give
+ * the same bits: t is rounded to fp16 once either way.
+ */
+int conv2d_dgrad_chain_nhwc_ws(const void* dy, const void* w1, const void* z, const void* w2, void* dx,
+                               int N, int H, int W, int Cm, int K, int R, int S, int pad, int C,
+                               int epilogue, void* workspace, size_t workspace_bytes, void* stream);
+
+/* *bytes = the workspace that lets conv2d_dgrad_chain_nhwc_ws choose the
+ * two-call path. Host-only. */
+int conv2d_dgrad_chain_workspace_size(int N, int H, int W, int Cm, int K, int R, int S, int pad, int C,
+                                      int epilogue, size_t* bytes);
+
+/* The path cached for a chain problem on the current device: *cached = 0 if
+ * none yet; *pair = 1 when the two-call path was found faster. */
+int conv2d_dgrad_chain_query(int N, int H, int W, int Cm, int K, int R, int S, int pad, int C,
+                             int epilogue, int* pair, int* cached);
 
 /* Validation alone (no HIP call) for conv2d_dgrad_chain_nhwc. */
 int conv2d_dgrad_chain_check(const void* dy, const void* w1, const void* z, const void* w2, const void* dx,

@@ -208,6 +208,188 @@ def test_invalid_call_returns_before_any_hip_call():
     assert e.value.code == cb.INVALID_ARGUMENT
 
 
+WS = 0x70000000   # a workspace address
+
+
+@pytest.mark.parametrize("ws,nbytes,code", [
+    (None, 16, cb.INVALID_ARGUMENT),            # NULL with a size
+    (WS + 8, 1 << 20, cb.INVALID_ARGUMENT),     # misaligned
+    (WS, 65535, cb.INVALID_ARGUMENT),           # smaller than the counter area
+    (DX - 4096, 1 << 20, cb.INVALID_ARGUMENT),  # overlaps dx
+    (DY + 256, 1 << 20, cb.INVALID_ARGUMENT),   # overlaps dy (512 bytes)
+])
+def test_workspace_validation(ws, nbytes, code):
+    for fn in (lambda: cb.conv2d_dgrad_nhwc_ws(DY, WP, DX, 2, 8, 8, 16, 8, 3, 3, 2, 1, workspace=(ws, nbytes),
+                                               stream=0),
+               lambda: cb.conv2d_dgrad_nhwc_config(DY, WP, DX, 2, 8, 8, 16, 8, 3, 3, 2, 1, config_id=0,
+                                                   workspace=(ws, nbytes), stream=0),
+               lambda: cb.conv2d_wgrad_nhwc_ws(DY, DX, WP, 2, 8, 8, 16, 8, 3, 3, 2, 1, workspace=(ws, nbytes),
+                                               stream=0)):
+        with pytest.raises(cb.DgradError) as e:
+            fn()
+        assert e.value.code == code and "workspace" in str(e.value)
+
+
+def test_workspace_size_queries():
+    from workloads import CONFIGS
+    sizes = {c.name: cb.conv2d_dgrad_workspace_size(c.N, c.H, c.W, c.C, c.K, c.R, c.S, c.stride, c.pad, c.epilogue)
+             for c in CONFIGS}
+    # layers whose tiles leave workgroups idle can split: counters + partial sums
+    assert sizes["tiny_n1_14x14_256_3x3_s1"] > 65536
+    assert sizes["r50_stage4_3x3_dhardswish_n256"] > 65536
+    # zero phases never split
+    assert sizes["r50_1x1_s2_downsample_n256"] == 0
+    for n in sizes.values():
+        assert n == 0 or 65536 < n <= 65536 + (1 << 30)
+    c = CONFIGS[2]
+    wsz = cb.conv2d_wgrad_workspace_size(c.N, c.H, c.W, c.C, c.K, c.R, c.S, c.stride, c.pad)
+    assert 65536 < wsz <= 65536 + (1 << 30)
+    assert cb.conv2d_wgrad_workspace_size(1, 1, 1, 8, 8, 1, 1, 1, 0) == 0   # one slice: nothing to split
+    with pytest.raises(cb.DgradError):
+        cb.conv2d_dgrad_workspace_size(2, 8, 8, 12, 8, 3, 3, 2, 1)
+
+
+def test_library_imports_no_allocator():
+    """The library never allocates device (or pinned host) memory: it imports
+    no allocation, free or memset routine of the HIP runtime."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", cb.LIB_PATH], check=True, capture_output=True,
+                         text=True).stdout
+    hip = [ln.split()[-1] for ln in out.splitlines() if "hip" in ln.lower()]
+    assert hip, "no HIP import found (nm output changed?)"
+    bad = [n for n in hip if re.search(r"alloc|free|memset|register", n, re.I) and "Fat" not in n
+           and "Function" not in n]
+    assert not bad, bad
+
+
+def test_library_sources_call_no_allocator():
+    csrc = os.path.join(ROOT, "convolution_backward_amd", "csrc")
+    for fn in os.listdir(csrc):
+        text = open(os.path.join(csrc, fn)).read()
+        text = re.sub(r"//[^\n]*", "", text)
+        assert not re.search(r"\bhip(Ext)?Malloc|\bhipFree|\bhipMemset|\bhipHostMalloc", text), fn
+
+
+def _meta(shape, dtype=None):
+    import torch
+    return torch.empty(shape, dtype=dtype or torch.float16, device="meta")
+
+
+@pytest.mark.parametrize("case", ["dy_pq", "w_k", "z_shape", "z_dtype", "out_shape", "out_dtype", "cpu"])
+def test_dgrad_wrapper_checks_shapes(case):
+    """Every tensor is checked against the shape the C call is told, before
+    any C call (a mismatch would let the kernel run past a buffer)."""
+    import torch
+    N, H, W, C, K = 2, 8, 8, 16, 8
+    dy, w = _meta((N, 4, 4, K)), _meta((K, 3, 3, C))        # stride 2, pad 1: P = Q = 4
+    z, out = _meta((N, H, W, C)), _meta((N, H, W, C))
+    kw = dict(epilogue=cb.EPI_DHARDSWISH, z=z, out=out)
+    if case == "dy_pq":
+        dy = _meta((N, 5, 4, K))
+    elif case == "w_k":
+        w = _meta((K + 8, 3, 3, C))
+    elif case == "z_shape":
+        kw["z"] = _meta((N, H, W - 1, C))
+    elif case == "z_dtype":
+        kw["z"] = _meta((N, H, W, C), torch.float32)
+    elif case == "out_shape":
+        kw["out"] = _meta((N, H, W, C + 8))
+    elif case == "out_dtype":
+        kw["out"] = _meta((N, H, W, C), torch.float32)
+    with pytest.raises(ValueError):
+        cb.dgrad(dy, w, H, W, 2, 1, **kw)
+
+
+@pytest.mark.parametrize("case", ["dy_pq", "out_shape", "out_dtype"])
+def test_wgrad_wrapper_checks_shapes(case):
+    import torch
+    dy, x = _meta((2, 4, 4, 8)), _meta((2, 8, 8, 16))
+    out = _meta((8, 3, 3, 16), torch.float32)
+    if case == "dy_pq":
+        dy = _meta((2, 4, 3, 8))
+    elif case == "out_shape":
+        out = _meta((8, 3, 3, 24), torch.float32)
+    elif case == "out_dtype":
+        out = _meta((8, 3, 3, 16))
+    with pytest.raises(ValueError):
+        cb.wgrad(dy, x, 3, 3, 2, 1, out=out)
+
+
+@pytest.mark.parametrize("case", ["bias", "out", "z_out", "w_c"])
+def test_forward_wrapper_checks_shapes(case):
+    x, w, bias = _meta((2, 8, 8, 16)), _meta((8, 3, 3, 16)), _meta((8,))
+    kw = dict(out=_meta((2, 4, 4, 8)), z_out=_meta((2, 4, 4, 8)))
+    if case == "bias":
+        bias = _meta((16,))
+    elif case == "out":
+        kw["out"] = _meta((2, 4, 5, 8))
+    elif case == "z_out":
+        kw["z_out"] = _meta((2, 4, 4, 16))
+    elif case == "w_c":
+        w = _meta((8, 3, 3, 24))
+    with pytest.raises(ValueError):
+        cb.forward(x, w, bias, 2, 1, **kw)
+
+
+@pytest.mark.parametrize("case", ["z", "out", "w2"])
+def test_chain_wrapper_checks_shapes(case):
+    dy, w1, w2 = _meta((2, 8, 8, 32)), _meta((32, 3, 3, 64)), _meta((64, 1, 1, 128))
+    z, out = _meta((2, 8, 8, 64)), _meta((2, 8, 8, 128))
+    if case == "z":
+        z = _meta((2, 8, 8, 128))
+    elif case == "out":
+        out = _meta((2, 8, 9, 128))
+    elif case == "w2":
+        w2 = _meta((64, 3, 1, 128))
+    with pytest.raises(ValueError):
+        cb.dgrad_chain(dy, w1, z, w2, 1, cb.EPI_DHARDSWISH, out=out)
+
+
+def test_table_under_concurrent_callers(tmp_path):
+    """Eight host threads query, save, load and clear the table at once
+    (ctypes releases the GIL in every call): no crash, every query answers,
+    and the table ends in a state one of the writers left."""
+    import threading
+    names = [cb.conv2d_dgrad_config_name(i) for i in range(cb.conv2d_dgrad_num_configs())]
+    lines = "".join(f"{n} 8 8 16 8 3 3 1 1 0 none 256 0 {names[n % len(names)]}\n" for n in range(1, 65))
+    src = tmp_path / "table.txt"
+    src.write_text(lines)
+    errors = []
+
+    def worker(k):
+        try:
+            for i in range(300):
+                op = (i + k) % 5
+                if op == 0:
+                    cid, _ = cb.conv2d_dgrad_query_config(1 + i % 64, 8, 8, 16, 8, 3, 3, 1, 1)
+                    assert 0 <= cid < len(names)
+                elif op == 1:
+                    cb.conv2d_dgrad_cache_load(str(src))
+                elif op == 2:
+                    cb.conv2d_dgrad_cache_save(str(tmp_path / f"out{k}.txt"))
+                elif op == 3 and i % 50 == 0:
+                    cb.conv2d_dgrad_cache_clear()
+                else:
+                    assert cb.conv2d_dgrad_workspace_size(1 + i % 64, 8, 8, 16, 8, 3, 3, 1, 1) >= 0
+                    assert 0 <= cb.conv2d_dgrad_cache_size() <= 64
+        except Exception as e:   # noqa: BLE001
+            errors.append(repr(e))
+
+    cb.conv2d_dgrad_cache_clear()
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
+    cb.conv2d_dgrad_cache_load(str(src))
+    assert cb.conv2d_dgrad_cache_size() == 64
+    for k in range(8):   # every saved file is a whole table: lines of 14 fields
+        for ln in (tmp_path / f"out{k}.txt").read_text().splitlines():
+            assert len(ln.split()) == 14
+    cb.conv2d_dgrad_cache_clear()
+
+
 def brute_phase(H, R, stride, pad, ph):
     """Taps reaching output rows h = ph + s*i, found by trying every r."""
     rows = list(range(ph, H, stride))
@@ -258,6 +440,7 @@ def test_plan_of_measured_layers():
 
 
 def test_query_config_without_gpu_uses_heuristic():
+    cb.conv2d_dgrad_cache_clear()
     cid, cached = cb.conv2d_dgrad_query_config(8, 56, 56, 64, 64, 3, 3, 1, 1)
     assert 0 <= cid < cb.conv2d_dgrad_num_configs() and not cached
     assert "x64x" in cb.conv2d_dgrad_config_name(cid)   # narrow layer -> 64-channel tile
@@ -269,14 +452,16 @@ def test_cache_save_load_roundtrip(tmp_path):
     # A saved line for a CPU-only host ("none", 256 CUs) is what a query here looks up.
     name = cb.conv2d_dgrad_config_name(1)
     f = tmp_path / "table.txt"
-    f.write_text(f"2 8 8 16 8 3 3 2 1 0 none 256 {name}\nthis line is ignored\n")
+    f.write_text(f"2 8 8 16 8 3 3 2 1 0 none 256 0 {name}\nthis line is ignored\n")
     cb.conv2d_dgrad_cache_load(str(f))
     assert cb.conv2d_dgrad_cache_size() == 1
     cid, cached = cb.conv2d_dgrad_query_config(2, 8, 8, 16, 8, 3, 3, 2, 1)
     assert cached and cid == 1
+    cid, cached = cb.conv2d_dgrad_query_config(2, 8, 8, 16, 8, 3, 3, 2, 1, with_workspace=True)
+    assert not cached   # calls with a workspace have their own entry
     out = tmp_path / "saved.txt"
     cb.conv2d_dgrad_cache_save(str(out))
-    assert out.read_text().split() == f"2 8 8 16 8 3 3 2 1 0 none 256 {name}".split()
+    assert out.read_text().split() == f"2 8 8 16 8 3 3 2 1 0 none 256 0 {name}".split()
     cb.conv2d_dgrad_cache_clear()
     assert cb.conv2d_dgrad_cache_size() == 0
 
@@ -289,18 +474,20 @@ def test_cache_keeps_stream_k_choice(tmp_path):
     split_ok = names.index("256x128x64/4x2")
     no_variant = names.index("256x64x64/4x1")
     f = tmp_path / "table.txt"
-    f.write_text(f"256 7 7 512 512 3 3 1 1 2 none 256 {names[split_ok]}+sk\n"
-                 f"2 8 8 16 8 3 3 2 1 0 none 256 {names[no_variant]}+sk\n"
-                 f"2 8 8 16 8 3 3 1 1 0 none 256 {names[no_variant]}\n")
+    f.write_text(f"256 7 7 512 512 3 3 1 1 2 none 256 1 {names[split_ok]}+sk\n"
+                 f"256 7 7 512 512 3 3 1 1 2 none 256 0 {names[split_ok]}+sk\n"     # a split needs a workspace
+                 f"2 8 8 16 8 3 3 2 1 0 none 256 1 {names[no_variant]}+sk\n"
+                 f"2 8 8 16 8 3 3 1 1 0 none 256 0 {names[no_variant]}\n")
     cb.conv2d_dgrad_cache_load(str(f))
     assert cb.conv2d_dgrad_cache_size() == 2
-    cid, cached = cb.conv2d_dgrad_query_config(256, 7, 7, 512, 512, 3, 3, 1, 1, cb.EPI_DHARDSWISH)
-    assert cached and cid == split_ok
+    cid, cached, split = cb.conv2d_dgrad_query_config(256, 7, 7, 512, 512, 3, 3, 1, 1, cb.EPI_DHARDSWISH,
+                                                      with_workspace=True, with_split=True)
+    assert cached and cid == split_ok and split
     out = tmp_path / "saved.txt"
     cb.conv2d_dgrad_cache_save(str(out))
     lines = sorted(out.read_text().splitlines())
-    assert lines == sorted([f"256 7 7 512 512 3 3 1 1 2 none 256 {names[split_ok]}+sk",
-                            f"2 8 8 16 8 3 3 1 1 0 none 256 {names[no_variant]}"])
+    assert lines == sorted([f"256 7 7 512 512 3 3 1 1 2 none 256 1 {names[split_ok]}+sk",
+                            f"2 8 8 16 8 3 3 1 1 0 none 256 0 {names[no_variant]}"])
     cb.conv2d_dgrad_cache_clear()
 
 

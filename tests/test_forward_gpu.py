@@ -93,27 +93,25 @@ def test_forward_without_z():
 
 @pytest.mark.parametrize("idx", range(1, len(CONFIGS)), ids=[c.name for c in CONFIGS[1:]])
 def test_forward_measured_layer(idx):
-    """Each measured layer's shape at full size (automatic config): sampled
-    output pixels against the oracle, the whole output checked for unwritten
-    elements, and the same bits on a second call."""
+    """Each measured layer's shape at full size (table-selected config): every
+    element of z and y against the oracle, and the same bits on a second
+    call."""
     cfg = CONFIGS[idx]
     x, w, b = _inputs(cfg, 54)
     note(f"forward measured layer {cfg.name}")
     z, y = run_forward(cfg, x, w, b, 1)
-    assert not np.isnan(z).any() and not np.isnan(y).any()
-    rng = np.random.Generator(np.random.PCG64(55 + idx))
-    npq = cfg.N * cfg.P * cfg.Q
-    rows = np.unique(np.concatenate([rng.choice(npq, size=min(400, npq), replace=False), [0, npq - 1]]))
-    zr, yr = oracle.forward(x, w, b, cfg.stride, cfg.pad, act=1, rows=rows)
-    assert_close(z.reshape(-1, cfg.K)[rows], zr, f"{cfg.name} z")
-    assert_close(y.reshape(-1, cfg.K)[rows], yr, f"{cfg.name} y")
+    zr, yr = oracle.forward(x, w, b, cfg.stride, cfg.pad, act=1)
+    assert_close(z, zr, f"{cfg.name} z")
+    assert_close(y, yr, f"{cfg.name} y")
+    del zr, yr
     z2, y2 = run_forward(cfg, x, w, b, 1)
     assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+    assert np.array_equal(z.view(np.uint16), z2.view(np.uint16))
 
 
 # x just below the 2^30-element limit (1x1 and strided 3x3), small-integer
 # inputs: z is exact and must equal the oracle's RNE fp16 value bit for bit
-# on sampled output pixels, including the last ones.
+# in every element.
 MAX_SHAPES = [
     ("x_1x1_s1", (63, 128, 128, 1024, 64, 1, 1, 1, 0)),       # x 1,056,964,608 elements
     ("x_3x3_s2", (40, 448, 448, 128, 64, 3, 3, 2, 1)),        # x 1,027,604,480 elements
@@ -131,7 +129,9 @@ def test_forward_maximum_sizes_bit_exact(name, shape):
     note(f"forward maximum size {name} {shape}")
     z, y = run_forward(cfg, x, w, b, 1)
     npq = cfg.N * cfg.P * cfg.Q
-    rows = np.unique(np.concatenate([rng.choice(npq, size=300, replace=False), np.arange(npq - 64, npq)]))
-    zr, yr = oracle.forward(x, w, b, cfg.stride, cfg.pad, act=1, rows=rows)
-    assert np.array_equal(z.reshape(-1, cfg.K)[rows], oracle.round_to_half(zr))
-    assert_close(y.reshape(-1, cfg.K)[rows], yr, f"{name} y")
+    zf, yf = z.reshape(-1, cfg.K), y.reshape(-1, cfg.K)
+    for p0 in range(0, npq, 1 << 20):    # chunks of output pixels keep host memory bounded
+        rows = np.arange(p0, min(npq, p0 + (1 << 20)), dtype=np.int64)
+        zr, yr = oracle.forward(x, w, b, cfg.stride, cfg.pad, act=1, rows=rows)
+        assert np.array_equal(zf[rows], oracle.round_to_half(zr)), f"z differs in pixels {p0}.."
+        assert_close(yf[rows], yr, f"{name} y pixels {p0}..")
