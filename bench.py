@@ -224,14 +224,13 @@ def main():
     # (4 MiB per XCD) and the 256 MiB Infinity Cache; the event pair on the
     # launch stream brackets the layer call alone
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
-    flush_out = torch.empty((), dtype=torch.float32, device=dev)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in layers] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         for li, (cfg, d) in enumerate(layers):
-            torch.sum(flush, out=flush_out)
+            flush.sum()
             ev[s][li][0].record(stream)
             one_layer(cfg, d)
             ev[s][li][1].record(stream)
@@ -261,7 +260,7 @@ def main():
         })
         log(f"[cold] {cfg.name:34s} {avg*1e3:9.2f} us  {per_layer[-1]['tflops']:7.1f} TFLOP/s  "
             f"{per_layer[-1]['alg_gbs']:7.0f} GB/s  {rl['bound']} {rl['frac']:.1%}  [{per_layer[-1]['tile_config']}]")
-    del flush, flush_out
+    del flush
 
     # ---- warm: the layers back to back (operands partly in the caches, like
     # the pages' nvprof averages), wall clock over the steps, then per-layer
