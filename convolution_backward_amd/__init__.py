@@ -47,6 +47,9 @@ def _bind(lib):
     lib.conv2d_dgrad_nhwc.argtypes = [vp, vp, vp] + [i] * 10 + [vp, vp]
     lib.conv2d_dgrad_nhwc_ws.argtypes = [vp, vp, vp] + [i] * 10 + [vp, vp, sz, vp]
     lib.conv2d_dgrad_workspace_size.argtypes = [i] * 10 + [szp]
+    lib.conv2d_dgrad_nhwc_noalloc.argtypes = [vp, vp, vp] + [i] * 10 + [vp, vp]
+    lib.conv2d_dgrad_noalloc_max_bytes.argtypes = []
+    lib.conv2d_dgrad_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.conv2d_dgrad_nhwc_config.argtypes = [vp, vp, vp] + [i] * 10 + [vp, i, vp, sz, vp]
     lib.conv2d_dgrad_num_configs.argtypes = []
     lib.conv2d_dgrad_config_name.argtypes = [i, ctypes.c_char_p, i]
@@ -81,7 +84,7 @@ def _bind(lib):
     lib.conv2d_dgrad_last_error.restype = ctypes.c_char_p
     lib.conv2d_dgrad_build_info.argtypes = []
     lib.conv2d_dgrad_build_info.restype = ctypes.c_char_p
-    for name in ("conv2d_dgrad_nhwc", "conv2d_dgrad_nhwc_ws", "conv2d_dgrad_workspace_size",
+    for name in ("conv2d_dgrad_nhwc", "conv2d_dgrad_nhwc_ws", "conv2d_dgrad_workspace_size", "conv2d_dgrad_nhwc_noalloc",
                  "conv2d_dgrad_nhwc_config", "conv2d_dgrad_num_configs",
                  "conv2d_dgrad_config_name", "conv2d_dgrad_query_config", "conv2d_dgrad_set_autotune",
                  "conv2d_dgrad_set_fault_inject", "conv2d_wgrad_nhwc_ws", "conv2d_wgrad_workspace_size",
@@ -163,6 +166,17 @@ def conv2d_dgrad_nhwc_ws(dy, w, dx, N, H, W, C, K, R, S, stride, pad, epilogue=E
     wp, wb = _ws(workspace)
     return _check(get_lib().conv2d_dgrad_nhwc_ws(_ptr(dy), _ptr(w), _ptr(dx), N, H, W, C, K, R, S, stride, pad,
                                                  epilogue, _ptr(z), wp, wb, _stream(stream, dy, dx)))
+
+
+def conv2d_dgrad_nhwc_noalloc(dy, w, dx, N, H, W, C, K, R, S, stride, pad, epilogue=EPI_NONE, z=None, stream=None):
+    """conv2d_dgrad_nhwc_ws with the library's static per-device scratch as the
+    workspace: allocates nothing (for callers that cannot allocate)."""
+    return _check(get_lib().conv2d_dgrad_nhwc_noalloc(_ptr(dy), _ptr(w), _ptr(dx), N, H, W, C, K, R, S, stride, pad,
+                                                      epilogue, _ptr(z), _stream(stream, dy, dx)))
+
+
+def conv2d_dgrad_noalloc_max_bytes() -> int:
+    return int(get_lib().conv2d_dgrad_noalloc_max_bytes())
 
 
 def conv2d_dgrad_workspace_size(N, H, W, C, K, R, S, stride, pad, epilogue=EPI_NONE) -> int:
@@ -567,6 +581,7 @@ def dgrad_chain(dy, w1, z, w2, pad, epilogue=EPI_NONE, out=None, workspace=None)
 
 __all__ = [
     "conv2d_dgrad_nhwc", "conv2d_dgrad_nhwc_ws", "conv2d_dgrad_workspace_size", "conv2d_dgrad_nhwc_config",
+    "conv2d_dgrad_nhwc_noalloc", "conv2d_dgrad_noalloc_max_bytes",
     "conv2d_dgrad_check", "conv2d_dgrad_num_configs",
     "conv2d_dgrad_config_name", "conv2d_dgrad_query_config", "conv2d_dgrad_set_autotune",
     "conv2d_dgrad_set_fault_inject", "conv2d_dgrad_set_streamk", "conv2d_dgrad_streamk_launches",

@@ -13,6 +13,13 @@ namespace cbw {
 // Phases per launch; strides above 4 are split over several launches.
 constexpr int kMaxPhasesPerLaunch = 16;
 
+// Bytes at the start of every workspace that hold arrival counters (one int32
+// per GEMM tile of a split launch); the rest holds partial sums.
+constexpr size_t kCounterBytes = 64 * 1024;
+
+// Device memory behind the no-allocation entry point (per device, static).
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+
 // One stride phase with taps, as the kernel sees it (see dgrad_plan.h for the algebra).
 struct PhaseArg {
     int ph, pw;          // lattice offsets
@@ -204,6 +211,14 @@ struct ChainArgs {
 hipError_t launch_chain(const ChainArgs& a, hipStream_t stream);
 int chain_private_bytes(int Cm, int epi);   // scratch bytes per lane, -1 if unknown
 int chain_lds_bytes(int Cm);
+
+// Zero fill of a device buffer (16-byte aligned, a multiple of 16 bytes).
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+// The no-allocation scratch of the current device (kNoAllocScratchBytes,
+// 256-byte aligned): its device address, found and its counter area cleared
+// (on `stream`) the first time per device.
+hipError_t noalloc_scratch(void** ptr, hipStream_t stream);
 
 int num_tile_configs();
 const TileConfig& tile_config(int id);

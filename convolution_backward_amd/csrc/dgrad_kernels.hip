@@ -49,6 +49,10 @@
 // pre-activation, fp32), rounds once to fp16 (RNE) and stores 8 bytes. dx is
 // never read. Zero phases (no tap reaches the lattice) store zeros with
 // 16-byte stores.
+#include <algorithm>
+#include <map>
+#include <mutex>
+
 #include "dgrad_internal.h"
 
 namespace cbw {
@@ -1042,6 +1046,78 @@ hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream)
     if (id < 0 || id >= kNumConfigs)
         return hipErrorInvalidValue;
     return kLaunch[id](a, stream);
+}
+
+// ============================================================ zero fill
+//
+// 16-byte zero stores over a buffer, one per thread in a grid-stride loop
+// (plain stores: the lines stay in the caches). Used to clear the no-
+// allocation scratch's counter area and, in the profiler, to push a layer's
+// operands out of the caches before a timed launch.
+
+namespace {
+
+__global__ void __launch_bounds__(256) fill_zero(u32x4* p, uint64_t n16)
+{
+    const u32x4 zero{0u, 0u, 0u, 0u};
+    for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < n16; i += (uint64_t)gridDim.x * 256u)
+        p[i] = zero;
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream)
+{
+    if (p == nullptr || ((uintptr_t)p & 15u) || (bytes & 15u))
+        return hipErrorInvalidValue;
+    const uint64_t n16 = bytes / 16;
+    if (n16 == 0)
+        return hipSuccess;
+    const uint64_t blocks = std::min<uint64_t>((n16 + 255) / 256, 8192);
+    hipLaunchKernelGGL(fill_zero, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4*)p, n16);
+    return hipGetLastError();
+}
+
+// ============================================================ no-allocation scratch
+//
+// The device memory of conv2d_dgrad_nhwc_noalloc, for callers that cannot
+// allocate: one static array per device, laid out like a caller's workspace
+// (arrival counters, then partial sums). Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol); it
+// passes the device address that hipGetSymbolAddress returned for the current
+// device, kept per device from the first use on.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_addr;   // device -> address of its copy of `scratch`
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr, hipStream_t stream)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_addr.find(dev);
+    if (it != g_scratch_addr.end()) {
+        *ptr = it->second;
+        return hipSuccess;
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return e;
+    if (p == nullptr || ((uintptr_t)p & 255u))
+        return hipErrorInvalidSymbol;
+    // the counters must start at zero (every launch leaves them so after that)
+    e = launch_fill_zero(p, kCounterBytes, stream);
+    if (e != hipSuccess)
+        return e;
+    g_scratch_addr[dev] = p;
+    *ptr = p;
+    return hipSuccess;
 }
 
 // ===================================================================== wgrad

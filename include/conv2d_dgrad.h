@@ -131,6 +131,29 @@ int conv2d_dgrad_workspace_size(int N, int H, int W, int C, int K, int R, int S,
                                 int stride, int pad, int epilogue, size_t* bytes);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * call as conv2d_dgrad_nhwc_ws, with the workspace taken from a static
+ * device array of the library, conv2d_dgrad_noalloc_max_bytes() = 128 MiB,
+ * which each GPU the library runs on holds until the process ends. Nothing
+ * is allocated, by the library or by the caller. The first call on a device
+ * looks up the array's address on that device and clears its counter area
+ * with a small kernel on `stream`. A problem whose split candidates need
+ * more than the array (see conv2d_dgrad_workspace_size) is rejected with
+ * CONV2D_DGRAD_UNSUPPORTED before anything is enqueued. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (different
+ * streams or host threads without ordering) race and may give wrong
+ * results; order them.
+ */
+int conv2d_dgrad_nhwc_noalloc(const void* dy, const void* w, void* dx,
+                              int N, int H, int W, int C, int K, int R, int S,
+                              int stride, int pad, int epilogue, const void* z,
+                              void* stream);
+
+/* Size of the static array behind conv2d_dgrad_nhwc_noalloc, in bytes. */
+size_t conv2d_dgrad_noalloc_max_bytes(void);
+
+/*
  * Same computation with an explicit tile configuration (0 <= config_id <
  * conv2d_dgrad_num_configs()), bypassing the table, and an optional
  * workspace as for conv2d_dgrad_nhwc_ws. For tests that check every
