@@ -38,64 +38,10 @@
 // Out-of-range accesses (padding taps, dead pixels past N*H*W, ragged K, Cm
 // or C) use the buffer range check: loads read zeros and stores are dropped.
 #include "dgrad_internal.h"
+#include "kernel_common.h"
 
 namespace cbw {
 namespace {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef float float16_t __attribute__((ext_vector_type(16)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// Raw 32-bit-format buffer accesses: a lane whose byte offset is at or past
-// the buffer size reads zeros and has its store dropped. Every tensor the host
-// admits is below 2^31 bytes, so 2^31 is out of range for all of them.
-constexpr int kChainBufferFlags = 0x00020000;
-constexpr int kChainStoreNT = 2;   // dx is written once: non-temporal
-
-__device__ inline __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kChainBufferFlags);
-}
-
-// `off` when bad == 0, exactly 2^31 when bad == 1 (arithmetic, no branch).
-__device__ inline uint32_t oor_if(uint32_t bad, uint32_t off)
-{
-    return (off & (bad - 1u)) | (bad << 31);
-}
-
-// Chunk (16-byte) permutation of pixel rows in LDS: chunk c of row m sits at
-// position c ^ ((m >> 1) & 7), so 16 lanes reading one chunk of 16
-// consecutive rows hit distinct 16-byte bank groups.
-__device__ inline int row_swizzle(int m)
-{
-    return (m >> 1) & 7;
-}
-
-// Chunk permutation of filter rows (2*width bytes): a transpose read covers,
-// per 32-lane half, four consecutive rows x four consecutive chunks; the
-// permutation spreads those over distinct bank groups.
-template <int ROW>
-__device__ inline int filt_swizzle(int k)
-{
-    static_assert(ROW == 128 || ROW == 256, "filter rows of 128 or 256 bytes");
-    return ROW == 128 ? 4 * ((k >> 1) & 1) : 4 * (k & 3);
-}
-
-template <int E>
-__device__ inline float chain_factor(float z)
-{
-    if constexpr (E == 0)
-        return 1.0f;
-    if constexpr (E == 1)
-        return z > 0.0f ? 1.0f : 0.0f;
-    const float mid = z / 3.0f + 0.5f;   // hardswish' on [-3, 3]; the division is correctly rounded
-    return z < -3.0f ? 0.0f : (z > 3.0f ? 1.0f : mid);
-}
 
 constexpr int kBM = 128;       // dx pixels per workgroup
 constexpr int kThreads = 512;  // 8 waves
@@ -116,15 +62,6 @@ struct ChainLayout {
     static constexpr int TOTAL = RING + kBM * T_ROW;
 };
 
-// Workgroup b runs on XCD b % 8 as its (b / 8)-th workgroup; give each XCD a
-// contiguous eighth of the tiles (a bijection on [0, tiles)).
-__device__ inline int chain_tile(int b, int tiles)
-{
-    const int x = b & 7, l = b >> 3;
-    const int q = tiles >> 3, r = tiles & 7;
-    return x * q + (x < r ? x : r) + l;
-}
-
 // NS1 > 0: stage 1 has exactly NS1 slices (taps x k steps), known at compile
 // time, and runs fully unrolled with a deeper prefetch; 0: any count.
 template <int CM, int E, int NS1>
@@ -141,13 +78,13 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
     const int wave = tid >> 6;
     const int wn = wave & 1;            // channel half
     const int wm = wave >> 1;           // pixel group of 32
-    const int tile = chain_tile(blockIdx.x, a.tiles);
+    const int tile = xcd_remap(blockIdx.x, a.tiles, 1, 1);   // each XCD a contiguous eighth of the tiles
     const int m0 = tile * kBM;
 
-    const __amdgpu_buffer_rsrc_t dy_r = chain_rsrc(a.dy, a.dy_bytes);
-    const __amdgpu_buffer_rsrc_t w1_r = chain_rsrc(a.w1, a.w1_bytes);
-    const __amdgpu_buffer_rsrc_t w2_r = chain_rsrc(a.w2, a.w2_bytes);
-    const __amdgpu_buffer_rsrc_t dx_r = chain_rsrc(a.dx, a.dx_bytes);
+    const __amdgpu_buffer_rsrc_t dy_r = make_rsrc(a.dy, a.dy_bytes);
+    const __amdgpu_buffer_rsrc_t w1_r = make_rsrc(a.w1, a.w1_bytes);
+    const __amdgpu_buffer_rsrc_t w2_r = make_rsrc(a.w2, a.w2_bytes);
+    const __amdgpu_buffer_rsrc_t dx_r = make_rsrc(a.dx, a.dx_bytes);
 
     // ---- stage-1 loader: dy chunks tid + 512*j, j < 2 (row tid/8 + 64*j, chunk tid%8)
     const int ld_chunk = tid & 7;
@@ -179,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
             const int p = ld_hp[j] - r, q = ld_wp[j] - s;
             const uint32_t bad = (uint32_t)!(((unsigned)p < (unsigned)a.P) & ((unsigned)q < (unsigned)a.Q) &
                                              (k0 + ld_chunk * 8 < a.K));
-            ldy[j] = __builtin_amdgcn_raw_buffer_load_b128(dy_r, oor_if(bad, (ld_base[j] - tapoff + (uint32_t)k0) * 2u), 0, 0);
+            ldy[j] = __builtin_amdgcn_raw_buffer_load_b128(dy_r, out_of_range_if(bad, (ld_base[j] - tapoff + (uint32_t)k0) * 2u), 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < W1_LD; ++j) {
@@ -188,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
             const int k = k0 + krow, c = cc * 8;
             const uint32_t bad = (uint32_t)((k >= a.K) | (c >= a.Cm));
             const uint32_t off = ((((uint32_t)k * (uint32_t)a.R + (uint32_t)r) * (uint32_t)a.S + (uint32_t)s) * (uint32_t)a.Cm + (uint32_t)c) * 2u;
-            lw1[j] = __builtin_amdgcn_raw_buffer_load_b128(w1_r, oor_if(bad, off), 0, 0);
+            lw1[j] = __builtin_amdgcn_raw_buffer_load_b128(w1_r, out_of_range_if(bad, off), 0, 0);
         }
     };
     auto store1 = [&](const u32x4 (&ldy)[2], const u32x4 (&lw1)[W1_LD], int buf) {
@@ -196,13 +133,13 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row = (tid >> 3) + 64 * j;
-            *(u32x4*)(st + row * 128 + ((ld_chunk ^ row_swizzle(row)) * 16)) = ldy[j];
+            *(u32x4*)(st + row * 128 + ((ld_chunk ^ dy_swizzle(row)) * 16)) = ldy[j];
         }
 #pragma unroll
         for (int j = 0; j < W1_LD; ++j) {
             const int i = tid + kThreads * j;
             const int krow = i / (CM / 8), cc = i % (CM / 8);
-            *(u32x4*)(st + L::DY_BYTES + krow * L::W1_ROW + ((cc ^ filt_swizzle<L::W1_ROW>(krow)) * 16)) = lw1[j];
+            *(u32x4*)(st + L::DY_BYTES + krow * L::W1_ROW + ((cc ^ w_swizzle<L::W1_ROW>(krow)) * 16)) = lw1[j];
         }
     };
 
@@ -215,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
     const int krow_a = (g >> 1) * 8 + rr;
     // Pixel-row operand (B): row wm*32 + lane%32, k chunk 2*kk + lane/32.
     const int prow = wm * 32 + (lane & 31);
-    const int psw = row_swizzle(prow);
+    const int psw = dy_swizzle(prow);
 
     auto tr_pair = [&](const char* p, int row_bytes) -> half8_t {
         const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(lds_char*)p);
@@ -230,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
 #pragma unroll
     for (int fn = 0; fn < FN1; ++fn) {
         const int cl = wn * (CM / 2) + fn * 32 + (g & 1) * 16 + 4 * qq;
-        a1_off[fn] = L::DY_BYTES + krow_a * L::W1_ROW + (((cl >> 3) ^ filt_swizzle<L::W1_ROW>(krow_a)) * 16) + (cl & 7) * 2;
+        a1_off[fn] = L::DY_BYTES + krow_a * L::W1_ROW + (((cl >> 3) ^ w_swizzle<L::W1_ROW>(krow_a)) * 16) + (cl & 7) * 2;
     }
     float16_t acc1[FN1];
 #pragma unroll
@@ -259,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
             const int row = i >> 4, cc = i & 15;
             const int cm = ks * 64 + row, ci = ch * kBN2 + cc * 8;
             const uint32_t bad = (uint32_t)((cm >= a.Cm) | (ci >= a.C));
-            rw2[j] = __builtin_amdgcn_raw_buffer_load_b128(w2_r, oor_if(bad, ((uint32_t)cm * (uint32_t)a.C + (uint32_t)ci) * 2u), 0, 0);
+            rw2[j] = __builtin_amdgcn_raw_buffer_load_b128(w2_r, out_of_range_if(bad, ((uint32_t)cm * (uint32_t)a.C + (uint32_t)ci) * 2u), 0, 0);
         }
     };
     auto store2 = [&](int buf) {
@@ -268,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
         for (int j = 0; j < 2; ++j) {
             const int i = tid + kThreads * j;
             const int row = i >> 4, cc = i & 15;
-            *(u32x4*)(st + row * L::W2_ROW + ((cc ^ filt_swizzle<L::W2_ROW>(row)) * 16)) = rw2[j];
+            *(u32x4*)(st + row * L::W2_ROW + ((cc ^ w_swizzle<L::W2_ROW>(row)) * 16)) = rw2[j];
         }
     };
     const int nch = (a.C + kBN2 - 1) / kBN2;
@@ -277,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
     u32x2 zr[FN1][4];
     auto load_z = [&]() {
         if constexpr (E != 0) {
-            const __amdgpu_buffer_rsrc_t z_r = chain_rsrc(a.z, a.z_bytes);
+            const __amdgpu_buffer_rsrc_t z_r = make_rsrc(a.z, a.z_bytes);
             const int m = m0 + prow;
 #pragma unroll
             for (int fn = 0; fn < FN1; ++fn)
@@ -285,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
                 for (int gq = 0; gq < 4; ++gq) {
                     const int c = wn * (CM / 2) + fn * 32 + 8 * gq + 4 * (lane >> 5);
                     const uint32_t bad = (uint32_t)((m >= a.M) | (c >= a.Cm));
-                    zr[fn][gq] = __builtin_amdgcn_raw_buffer_load_b64(z_r, oor_if(bad, ((uint32_t)m * (uint32_t)a.Cm + (uint32_t)c) * 2u), 0, 0);
+                    zr[fn][gq] = __builtin_amdgcn_raw_buffer_load_b64(z_r, out_of_range_if(bad, ((uint32_t)m * (uint32_t)a.Cm + (uint32_t)c) * 2u), 0, 0);
                 }
         }
     };
@@ -366,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
                     const half4_t zh = __builtin_bit_cast(half4_t, zr[fn][gq]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        tv[fn][gq][i] = (_Float16)(acc1[fn][4 * gq + i] * chain_factor<E>((float)zh[i]));
+                        tv[fn][gq][i] = (_Float16)(acc1[fn][4 * gq + i] * epilogue_factor<E>((float)zh[i]));
                 }
         } else {
 #pragma unroll
@@ -382,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int c = wn * (CM / 2) + fn * 32 + 8 * gq + 4 * (lane >> 5);
-                *(half4_t*)(lds + L::T_OFF + px * L::T_ROW + (((c >> 3) ^ row_swizzle(px)) * 16) + (c & 7) * 2) = tv[fn][gq];
+                *(half4_t*)(lds + L::T_OFF + px * L::T_ROW + (((c >> 3) ^ dy_swizzle(px)) * 16) + (c & 7) * 2) = tv[fn][gq];
             }
     }
     store2(0);
@@ -393,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn) {
         const int cl = wn * 64 + fn * 32 + (g & 1) * 16 + 4 * qq;
-        a2_off[fn] = krow_a * L::W2_ROW + (((cl >> 3) ^ filt_swizzle<L::W2_ROW>(krow_a)) * 16) + (cl & 7) * 2;
+        a2_off[fn] = krow_a * L::W2_ROW + (((cl >> 3) ^ w_swizzle<L::W2_ROW>(krow_a)) * 16) + (cl & 7) * 2;
     }
     float16_t acc2[2];
     acc2[0] = float16_t{};
@@ -436,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
             const int m = m0 + wm * 32 + row;
             const int ci = ch * kBN2 + wn * 64 + cc * 8;
             const uint32_t bad = (uint32_t)((m >= a.M) | (ci >= a.C));
-            __builtin_amdgcn_raw_buffer_store_b128(v, dx_r, oor_if(bad, ((uint32_t)m * (uint32_t)a.C + (uint32_t)ci) * 2u), 0, kChainStoreNT);
+            __builtin_amdgcn_raw_buffer_store_b128(v, dx_r, out_of_range_if(bad, ((uint32_t)m * (uint32_t)a.C + (uint32_t)ci) * 2u), 0, kStoreNT);
         }
     };
     for (int u = 0; u < ns2; ++u) {

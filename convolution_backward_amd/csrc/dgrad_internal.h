@@ -119,6 +119,8 @@ struct TileConfig {
     int lds_bytes;
     bool streamk;        // compiled with a stream-K variant
     bool phase_order;    // supports tile order 2 (phases of a pixel block side by side)
+    bool plain_only;     // runs launches of GEMM tiles only, one tile per workgroup (dgrad_wide);
+                         // the host gives launches with zero phases to plain_fallback(id)
 };
 
 // ------------------------------------------------------------------ wgrad
@@ -220,8 +222,17 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 // (on `stream`) the first time per device.
 hipError_t noalloc_scratch(void** ptr, hipStream_t stream);
 
+// The configurations of dgrad_wide (dgrad_wide.hip), numbered after those of
+// dgrad_igemm in the table of every configuration.
+int wide_num_configs();
+const TileConfig& wide_config(int i);
+hipError_t launch_wide(int i, const KernelArgs& a, hipStream_t stream);
+int wide_blocks_per_cu(int i);
+int wide_private_bytes(int i);
+
 int num_tile_configs();
 const TileConfig& tile_config(int id);
+int plain_fallback(int id);   // for a plain_only config: the dgrad_igemm config of the same tile
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);
 int blocks_per_cu(int id);   // resident workgroups per CU (current device)
 int kernel_private_bytes(int id);   // scratch bytes per lane of a config's kernel (-1: unknown)

@@ -54,39 +54,10 @@
 #include <mutex>
 
 #include "dgrad_internal.h"
+#include "kernel_common.h"
 
 namespace cbw {
 namespace {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef float float16_t __attribute__((ext_vector_type(16)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// Buffer resources for raw, unswizzled 32-bit-format buffer accesses. A lane
-// whose offset is at or past the buffer size reads zeros and has its store
-// dropped by the hardware range check; 2^31 is such an offset for every
-// tensor the host admits (all are below 2^31 bytes).
-constexpr int kRawBufferFlags = 0x00020000;
-
-// Byte offset for a buffer access: `off` itself (below 2^31 for an in-range
-// lane), or exactly 2^31 when bad == 1. Arithmetic, not a select, so no branch
-// is formed around the access. A caller may add up to 2^31 - 1 more bytes to
-// a bad offset and still stay out of range without wrapping.
-__device__ inline uint32_t out_of_range_if(uint32_t bad, uint32_t off)
-{
-    return (off & (bad - 1u)) | (bad << 31);
-}
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferFlags);
-}
 
 // The kernel's arguments, read again from the kernarg segment where they are
 // used. The empty asm keeps the compiler from hoisting these loads, so that
@@ -98,116 +69,6 @@ __device__ inline const __attribute__((address_space(4))) KernelArgs* kernargs()
     asm volatile("" : "+s"(p));
     return p;
 }
-
-// The same descriptor as four dwords (base, stride 0, size, format), for the
-// inline-assembly loads.
-__device__ inline i32x4 raw_descriptor(const void* base, uint32_t bytes)
-{
-    const uint64_t p = (uint64_t)base;
-    return i32x4{(int)(uint32_t)p, (int)((p >> 32) & 0xffffu), (int)bytes, kRawBufferFlags};
-}
-
-// One 16-byte direct-to-LDS load per lane: LDS[lds_base + 16*lane] <-
-// buffer[voffset + soffset] (soffset wave-uniform). An in-range lane has
-// voffset + soffset inside the buffer; an out-of-range lane has voffset =
-// 2^31 (and soffset < 2^31), outside the buffer however the hardware combines
-// the two offsets for its range check.
-__device__ inline void dma16(i32x4 desc, uint32_t voffset, uint32_t soffset, uint32_t lds_base)
-{
-    const int so = __builtin_amdgcn_readfirstlane((int)soffset);   // uniform by construction
-    const int lb = __builtin_amdgcn_readfirstlane((int)lds_base);
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 :
-                 : "v"(voffset), "s"(desc), "s"(so), "s"(lb)
-                 : "memory", "m0");
-}
-
-// A wave-uniform 32-bit value kept in a scalar register: the compiler may
-// not re-derive it later from the kernel arguments (a scalar memory load,
-// whose wait would also drain the LDS reads in flight). The value is taken
-// from the first active lane, which is exact for a uniform value wherever the
-// compiler happened to hold it.
-template <typename T>
-__device__ inline T pin(T x)
-{
-    static_assert(sizeof(T) == 4, "32-bit values");
-    int v = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x));
-    asm volatile("" : "+s"(v));
-    return __builtin_bit_cast(T, v);
-}
-
-template <int N>
-__device__ inline void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-__device__ inline int dy_swizzle(int row)
-{
-    return (row >> 1) & 7;
-}
-
-// Chunk permutation of filter row k in LDS (rows of 2*BN bytes). A
-// transpose read covers, per 32-lane half, four consecutive rows x four
-// consecutive chunks; the permutation sends these 16 (row, chunk) pairs to
-// 16 distinct 16-byte bank groups of the 256-byte bank window.
-template <int B_ROW>
-__device__ inline int w_swizzle(int k)
-{
-    static_assert(B_ROW == 128 || B_ROW % 256 == 0, "filter rows of 128 bytes or whole bank windows");
-    return B_ROW == 128 ? 4 * ((k >> 1) & 1) : 4 * (k & 3);
-}
-
-// Cache policy of the dx stores: non-temporal. dx is written once and never
-// read back here, so its lines should not displace dy and filter lines in L2
-// (measured: 4-13% per layer).
-constexpr int kStoreNT = 2;
-
-constexpr int kEpiNone = 0;
-constexpr int kEpiDRelu = 1;
-constexpr int kEpiDHardswish = 2;
-
-// Hardware dispatch places workgroup b on XCD (b mod 8) as that XCD's
-// (b div 8)-th workgroup; each XCD has its own L2. Two placements:
-//   mode 0: each XCD gets whole groups of `g` consecutive logical tiles
-//           (tiles that share operands, e.g. the channel tiles of one pixel
-//           block), groups rotating over the XCDs so a heavy-first phase
-//           order stays balanced; a tail that fills no 8 groups is unchanged.
-//   mode 1: each XCD gets one contiguous eighth of the logical tiles (for a
-//           single phase whose tiles are ordered pixel-block fastest, an XCD
-//           then works on as few filter slices as possible).
-__device__ inline int xcd_remap(int b, int total, int g, int mode)
-{
-    const int x = b & 7;
-    const int l = b >> 3;
-    if (mode == 1) {
-        const int q = total >> 3, r = total & 7;
-        return x * q + (x < r ? x : r) + l;
-    }
-    const int span = 8 * g;
-    const int main_part = (total / span) * span;
-    if (b >= main_part)
-        return b;
-    return ((l / g) * 8 + x) * g + (l % g);
-}
-
-// g(z) for the fused epilogues, evaluated in fp32 without branches.
-// relu'(z) = [z > 0]; hardswish'(z) = 0 below -3, z/3 + 1/2 on the closed
-// interval [-3, 3], 1 above 3 (the division is correctly rounded).
-template <int E>
-__device__ inline float epilogue_factor(float z)
-{
-    if constexpr (E == kEpiDRelu)
-        return z > 0.0f ? 1.0f : 0.0f;
-    const float mid = z / 3.0f + 0.5f;
-    return z < -3.0f ? 0.0f : (z > 3.0f ? 1.0f : mid);
-}
-
-template <int E>
-struct EpiTag {
-    static constexpr int value = E;
-};
 
 // The phase-interleaved tile order (order 2) exists for every configuration
 // but 256x64/4x1, whose scalar registers are full without it.
@@ -988,7 +849,7 @@ int resident(void)
 
 #define CBW_CONFIG_ENTRY(BM, BN, WM, WN) \
     {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN, 3 * (BM + BN) * 64 * 2, kHasStreamK<BM, BN, WM, WN>, \
-     kHasPhaseOrder<BM, BN, WM, WN>},
+     kHasPhaseOrder<BM, BN, WM, WN>, false},
 const TileConfig kConfigs[] = {CBW_TILE_CONFIGS(CBW_CONFIG_ENTRY)};
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs <= 64, "the launcher keeps per-config state for at most 64 configs");
@@ -1027,25 +888,44 @@ const ResidentFn kPrivate[] = {CBW_TILE_CONFIGS(CBW_PRIVATE_ENTRY)};
 
 }  // namespace
 
-int num_tile_configs() { return kNumConfigs; }
+// Configuration ids: dgrad_igemm's first, then dgrad_wide's.
+int num_tile_configs() { return kNumConfigs + wide_num_configs(); }
 
-const TileConfig& tile_config(int id) { return kConfigs[id]; }
+const TileConfig& tile_config(int id) { return id < kNumConfigs ? kConfigs[id] : wide_config(id - kNumConfigs); }
+
+int plain_fallback(int id)
+{
+    const TileConfig& tc = tile_config(id);
+    if (!tc.plain_only)
+        return id;
+    int best = 0;
+    for (int i = 0; i < kNumConfigs; ++i)
+        if (kConfigs[i].BM == tc.BM && kConfigs[i].BN == tc.BN)
+            best = i;
+    return best;
+}
 
 int blocks_per_cu(int id)
 {
-    return (id >= 0 && id < kNumConfigs) ? kResident[id]() : 1;
+    if (id >= 0 && id < kNumConfigs)
+        return kResident[id]();
+    return wide_blocks_per_cu(id - kNumConfigs);
 }
 
 int kernel_private_bytes(int id)
 {
-    return (id >= 0 && id < kNumConfigs) ? kPrivate[id]() : -1;
+    if (id >= 0 && id < kNumConfigs)
+        return kPrivate[id]();
+    return wide_private_bytes(id - kNumConfigs);
 }
 
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream)
 {
-    if (id < 0 || id >= kNumConfigs)
+    if (id < 0 || id >= num_tile_configs())
         return hipErrorInvalidValue;
-    return kLaunch[id](a, stream);
+    if (id < kNumConfigs)
+        return kLaunch[id](a, stream);
+    return launch_wide(id - kNumConfigs, a, stream);
 }
 
 // ============================================================ zero fill

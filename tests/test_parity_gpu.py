@@ -70,6 +70,36 @@ def test_small_epilogues(small_refs, shape, epi):
     assert_close(run(cfg, inp, config_id=0), ref, f"{shape} epi {epi} config 0")
 
 
+def _wide_configs():
+    return [cid for cid in range(cb.conv2d_dgrad_num_configs()) if cb.conv2d_dgrad_config_name(cid).endswith("w")]
+
+
+# Shapes without zero phases (the one-tile-per-workgroup kernel runs them
+# itself): ragged M, C and K, several phases, a pixel tile past the end, a
+# single pixel, 5x5 and 7x7 filters.
+WIDE_SHAPES = [
+    (2, 15, 13, 136, 72, 3, 3, 1, 1),
+    (2, 17, 16, 64, 128, 3, 3, 2, 1),
+    (2, 9, 9, 16, 16, 5, 5, 3, 2),
+    (1, 14, 14, 264, 56, 1, 1, 1, 0),
+    (1, 5, 5, 8, 8, 7, 7, 1, 3),
+    (1, 1, 1, 8, 8, 1, 1, 1, 0),
+    (4, 28, 28, 192, 320, 3, 3, 1, 1),
+    (3, 7, 7, 512, 136, 3, 3, 1, 1),
+]
+
+
+@pytest.mark.parametrize("epi", [EPI_NONE, EPI_DRELU, EPI_DHARDSWISH])
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_wide_kernel_every_epilogue(shape, epi):
+    cfg = _cfg(shape, epi, seed=9)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in _wide_configs():
+        note(f"wide kernel {shape} epilogue {epi} config {cid}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} epi {epi} config {cid}")
+
+
 # ---------------------------------------------------------------- full sizes
 
 @pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
@@ -136,7 +166,7 @@ def test_fused_layer_streamk_forced_bit_exact():
     try:
         for cid in range(cb.conv2d_dgrad_num_configs()):
             name = cb.conv2d_dgrad_config_name(cid)
-            if name == "256x64x64/4x1":
+            if name == "256x64x64/4x1" or name.endswith("w"):
                 continue   # no stream-K variant
             before = cb.conv2d_dgrad_streamk_launches()
             note(f"fused layer, stream-K forced, config {cid} {name}")
