@@ -61,6 +61,19 @@ def roofline_of(cfg, seconds):
             "frac": achieved / HBM_PEAK_GBS}
 
 
+KERNEL_SOURCES = ("dgrad_kernels.hip", "dgrad_wide.hip", "kernel_common.h", "dgrad_internal.h")
+
+
+def kernel_source_digest():
+    """First 16 hex digits of the SHA-256 of the dgrad kernel sources, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "convolution_backward_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(kernel_key):
     """HBM bytes per launch from the committed rocprofv3 counter summary, when
     it was taken on the current kernel source; else None."""
@@ -69,10 +82,7 @@ def measured_traffic(kernel_key):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    import hashlib
-    src = os.path.join(ROOT, "convolution_backward_amd", "csrc", "dgrad_kernels.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if t.get("kernel_source_sha256_16") != digest:
+    if t.get("kernel_source_sha256_16") != kernel_source_digest():
         return None
     entry = t.get("layers", {}).get(kernel_key)
     return None if entry is None else entry.get("bytes_per_launch")
@@ -437,8 +447,19 @@ def main():
             ms = [e0.elapsed_time(e1) for e0, e1 in evs]
             return float(np.mean(ms)), float(np.min(ms))
 
+        cws = cb.workspace(cb.conv2d_dgrad_chain_workspace_size(ccfg.N, ccfg.H, ccfg.W, ccfg.Cm, ccfg.K, ccfg.R,
+                                                                ccfg.S, ccfg.pad, ccfg.C, ccfg.epilogue), dev)
+
+        def chosen():
+            cb.conv2d_dgrad_chain_nhwc_ws(ci["dy"], ci["w1"], ci["z"], ci["w2"], cdx, ccfg.N, ccfg.H, ccfg.W,
+                                          ccfg.Cm, ccfg.K, ccfg.R, ccfg.S, ccfg.pad, ccfg.C, ccfg.epilogue, cws,
+                                          stream.cuda_stream)
+
         f_avg, f_min = timed(fused)
         p_avg, p_min = timed(pair)
+        c_avg, c_min = timed(chosen)
+        use_pair, _ = cb.conv2d_dgrad_chain_query(ccfg.N, ccfg.H, ccfg.W, ccfg.Cm, ccfg.K, ccfg.R, ccfg.S, ccfg.pad,
+                                                  ccfg.C, ccfg.epilogue)
         fl = ccfg.useful_flops()
         nbytes = ccfg.algorithmic_bytes()
         t_bytes = 2 * 2 * ccfg.N * ccfg.H * ccfg.W * ccfg.Cm     # t written and read back by the pair
@@ -453,11 +474,15 @@ def main():
                          "pair = two dgrad calls with t in HBM",
                  "workload": ccfg.name, "fused_us": f_avg * 1e3, "fused_min_us": f_min * 1e3,
                  "pair_us": p_avg * 1e3, "pair_min_us": p_min * 1e3, "speedup": p_avg / f_avg,
+                 "chosen": "pair" if use_pair else "fused", "chosen_us": c_avg * 1e3,
+                 "chosen_note": "conv2d_dgrad_chain_nhwc_ws with a workspace that holds t: the library times both "
+                                "paths on the first call and keeps the faster",
                  "tflops": fl / (f_avg * 1e-3) / 1e12, "alg_mb": nbytes / 1e6,
                  "pair_alg_mb": (nbytes + t_bytes) / 1e6, "roofline": rl}
         log(f"[chain] {ccfg.name:34s} fused {f_avg*1e3:9.2f} us  pair {p_avg*1e3:9.2f} us  "
-            f"{chain['tflops']:7.1f} TFLOP/s  {rl['bound']} {rl['frac']:.1%}")
-        del ci, cdx, ct, cdx2
+            f"chosen ({chain['chosen']}) {c_avg*1e3:9.2f} us  {chain['tflops']:7.1f} TFLOP/s  "
+            f"{rl['bound']} {rl['frac']:.1%}")
+        del ci, cdx, ct, cdx2, cws
         return chain
 
     chain = chain3 = None
@@ -475,6 +500,7 @@ def main():
     roof["unit_of_work"] = ("one layer call = one launch; algorithmic bytes dy + w + dx (+ z), each once, "
                             f"{dcfg.algorithmic_bytes()} B; cold mean of {args.steps} launches")
     roof["traffic"] = measured_traffic(dcfg.name)
+    roof["kernel_source_sha256_16"] = kernel_source_digest()
 
     cpu = None
     if args.cpu_fraction > 0:

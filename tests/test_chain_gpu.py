@@ -110,6 +110,36 @@ def test_chain_matches_the_unfused_pair_on_integer_inputs():
     assert np.array_equal(fused.view(np.uint16), dx.cpu().numpy().view(np.uint16))
 
 
+def test_chain_with_workspace_chooses_a_path():
+    """With a workspace that holds t, the first call times the fused kernel
+    against the two-call pair and caches the faster; whichever runs, the
+    result is bit-exact against the oracle on integer inputs (t is rounded to
+    fp16 once on both paths), and a workspace too small for t keeps the
+    fused kernel."""
+    import torch
+    for shape in [(2, 14, 13, 64, 64, 3, 3, 1, 256), (1, 9, 11, 128, 32, 3, 3, 1, 136)]:
+        cfg = _cfg(shape, cb.EPI_DHARDSWISH, seed=41)
+        inp = integer_chain_inputs(cfg, seed=13)
+        want = oracle.round_to_half(oracle.chain(inp["dy"], inp["w1"], inp["z"], inp["w2"], cfg.H, cfg.W, cfg.pad,
+                                                 cfg.epilogue))
+        need = cb.conv2d_dgrad_chain_workspace_size(cfg.N, cfg.H, cfg.W, cfg.Cm, cfg.K, cfg.R, cfg.S, cfg.pad, cfg.C,
+                                                    cfg.epilogue)
+        assert need >= 65536 + 2 * cfg.N * cfg.H * cfg.W * cfg.Cm
+        d = {k: to_dev(v) for k, v in inp.items()}
+        for ws_bytes in (need, 65536 + 256):
+            ws = cb.workspace(ws_bytes)
+            for rep in range(2):   # the first call may time both paths into dx; the second runs the choice
+                dx = torch.full((cfg.N, cfg.H, cfg.W, cfg.C), float("nan"), dtype=torch.float16, device="cuda")
+                note(f"chain with workspace {ws_bytes} {shape} call {rep}")
+                cb.dgrad_chain(d["dy"], d["w1"], d["z"], d["w2"], cfg.pad, cfg.epilogue, out=dx, workspace=ws)
+                torch.cuda.synchronize()
+                got = dx.cpu().numpy()
+                assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), f"{shape} ws {ws_bytes}"
+        pair, cached = cb.conv2d_dgrad_chain_query(cfg.N, cfg.H, cfg.W, cfg.Cm, cfg.K, cfg.R, cfg.S, cfg.pad, cfg.C,
+                                                   cfg.epilogue)
+        assert cached
+
+
 def test_chain_deterministic():
     cfg = _cfg(SMALL[0], cb.EPI_DHARDSWISH)
     inp = make_chain_inputs(cfg)

@@ -8,6 +8,8 @@ import subprocess
 
 import pytest
 
+from convolution_backward_amd.build import SOURCES
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "convolution_backward_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -17,8 +19,7 @@ pytestmark = pytest.mark.slow
 
 def test_abi_under_asan_ubsan_with_eight_threads(tmp_path):
     exe = str(tmp_path / "abi_stress")
-    sources = [os.path.join(ROOT, "tests", "abi_stress.cpp")] + [
-        os.path.join(CSRC, f) for f in ("dgrad_api.cpp", "dgrad_plan.cpp", "dgrad_kernels.hip", "chain_kernels.hip")]
+    sources = [os.path.join(ROOT, "tests", "abi_stress.cpp")] + [os.path.join(CSRC, f) for f in SOURCES]
     cmd = [HIPCC, "-O1", "-g", "-std=c++17", "--offload-arch=gfx950",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
