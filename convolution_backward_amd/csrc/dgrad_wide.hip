@@ -17,6 +17,11 @@
 // Each workgroup owns one tile (the grid is the tile count, one workgroup per
 // CU at a time for LDS reasons), which keeps the wave-uniform state small
 // enough for the scalar register file.
+//
+// The fused epilogues' z tile (BM pixels x BN channels, fp16) travels to LDS
+// during the last two slices, into the stages that no slice needs any more,
+// so its load latency hides behind matrix-core work instead of opening the
+// epilogue.
 #include "dgrad_internal.h"
 #include "kernel_common.h"
 
@@ -122,48 +127,114 @@ dgrad_wide(KernelArgs a)
         b_k[jn] = k;
         w_vt[jn] = c0 + cc >= C ? 0x80000000u : (uint32_t)(k * RSC + cc) * 2u;
     }
-    int ar = 0, at = 0, k0 = 0;   // request cursor: row tap, column tap, k step
+    auto pixel_offset = [&](int m) __attribute__((always_inline)) -> uint32_t {   // dx element offset of lattice row m
+        const uint32_t n = fastdiv((uint32_t)m, ph.div_hw);
+        const uint32_t rem = (uint32_t)m - n * ph.div_hw.d;
+        const uint32_t i = fastdiv(rem, ph.div_w);
+        const uint32_t j = rem - i * (uint32_t)ph.Wp;
+        const uint32_t pix = (n * (uint32_t)a.H + (uint32_t)(ph.ph + s * (int)i)) * (uint32_t)a.W
+                             + (uint32_t)(ph.pw + s * (int)j);
+        return pix * (uint32_t)C;
+    };
+
+    // ---- the request stream: items 0..niter-1 are the slices; items niter
+    // and niter + 1 carry the fused epilogue's z tile (BM pixels x BN
+    // channels), each as one slice's worth of loads. Item j goes to stage
+    // j mod 3 like a slice, so z lands in the two stages no slice needs any
+    // more while the last two slices run, and its latency hides behind them.
+    // Without z (or past its end) the lanes are out of range and write zeros.
+    // Load X of an item fills this wave's block X*NW + wave of the stage
+    // (blocks 0..A_INSTR*NW-1 are the dy rows of a slice, the rest its filter
+    // rows). In the z items, 1 KiB block b holds z rows ZRPB*b.., row p's
+    // chunk c at position c ^ (p % ZCH); item niter holds blocks
+    // 0..LD*NW-1, item niter + 1 the rest.
+    constexpr int ZROW = BN * 2;
+    constexpr int ZCH = ZROW / 16;                   // chunks per z row
+    constexpr int ZRPB = 1024 / ZROW;                // rows per 1 KiB block
+    constexpr int ZX = BM * ZROW / 1024 / NW;        // z blocks per wave
+    constexpr int ZA_ROWS = LD * NW * ZRPB;          // rows in item niter
+    static_assert(ZROW <= 1024 && 1024 % ZROW == 0 && 64 % ZCH == 0, "whole z rows per block");
+    static_assert((BM * ZROW / 1024) % NW == 0, "whole z blocks per wave");
+    static_assert(ZX > LD && ZX <= 2 * LD, "the z tile spans the two items");
+    static_assert(A_BYTES == A_INSTR * NW * 1024, "block X of a stage at X*NW KiB");
+    const bool zpre = a.epi != kEpiNone;
+    const int zstage_a = niter % 3, zstage_b = (niter + 1) % 3;
+    const i32x4 z_desc = raw_descriptor(zpre ? a.z : a.dx, a.dx_bytes);
+    auto z_offset = [&](int x) __attribute__((always_inline)) -> uint32_t {          // this lane's z byte offset in block x*NW + wave
+        const int row = (x * NW + wave) * ZRPB + lane / ZCH;
+        const int c = ((lane % ZCH) ^ (row % ZCH)) * 8;
+        const int m = m0 + row;
+        const uint32_t bad = (uint32_t)(!zpre) | (uint32_t)(x >= ZX) | (uint32_t)(m >= ph.M) | (uint32_t)(c0 + c >= C);
+        const uint32_t off = bad ? 0u : (pixel_offset(m) + (uint32_t)(c0 + c)) * 2u;
+        return out_of_range_if(bad, off);
+    };
+    auto z_row_lds = [&](int p) __attribute__((always_inline)) -> int {            // LDS byte offset of z row p
+        return p < ZA_ROWS ? zstage_a * STAGE + p * ZROW : zstage_b * STAGE + (p - ZA_ROWS) * ZROW;
+    };
+
+    int item = 0;                 // the next item to prepare
+    int ar = 0, at = 0, k0 = 0;   // slice cursor: row tap, column tap, k step
     bool new_tap = true;
     uint32_t q_wtap = 0;          // filter byte offset of the current tap (wave-uniform)
-    uint32_t q_base = 0;          // LDS address of the stage being filled
-    auto prepare = [&](int buf) {
-        if (new_tap) {            // once per tap: padding checks and dy offsets
-            new_tap = false;
-            const int dr = dr0 - ar;
-            const int dt = dt0 - at;
-            const uint32_t tapoff = (uint32_t)((dr * Q + dt) * K) * 2u;
+    // the prepared item's descriptors and scalar offsets: dy-block loads (a)
+    // and filter-block loads (b)
+    i32x4 desc_a = dy_desc, desc_b = w_desc;
+    uint32_t so_a = 0, so_b = 0;
+    // LDS address of this wave's first block; block X of stage st lies a
+    // compile-time distance further (m0 is formed with one add)
+    const uint32_t dma_base = pin(lds_u32 + (uint32_t)(wave * 1024));
+    auto prepare = [&]() __attribute__((always_inline)) {
+        if (item < niter) {
+            if (new_tap) {        // once per tap: padding checks and dy offsets
+                new_tap = false;
+                const int dr = dr0 - ar;
+                const int dt = dt0 - at;
+                const uint32_t tapoff = (uint32_t)((dr * Q + dt) * K) * 2u;
 #pragma unroll
-            for (int jn = 0; jn < A_INSTR; ++jn) {
-                const bool ok = ((unsigned)(a_i[jn] + dr) < (unsigned)P) & ((unsigned)(a_j[jn] + dt) < (unsigned)Q);
-                dy_vo[jn] = ok ? a_off[jn] + tapoff : 0x80000000u;
+                for (int jn = 0; jn < A_INSTR; ++jn) {
+                    const bool ok = ((unsigned)(a_i[jn] + dr) < (unsigned)P) & ((unsigned)(a_j[jn] + dt) < (unsigned)Q);
+                    dy_vo[jn] = ok ? a_off[jn] + tapoff : 0x80000000u;
+                }
+#pragma unroll
+                for (int jn = 0; jn < B_INSTR; ++jn)
+                    w_vo[jn] = w_vt[jn];
+                q_wtap = (uint32_t)(wt0 + ar * s * SC + at * s * C) * 2u;
             }
+            if (k0 + BK > K) {    // ragged last k step of a tap: mask the lanes past K
 #pragma unroll
-            for (int jn = 0; jn < B_INSTR; ++jn)
-                w_vo[jn] = w_vt[jn];
-            q_wtap = (uint32_t)(wt0 + ar * s * SC + at * s * C) * 2u;
-        }
-        if (k0 + BK > K) {        // ragged last k step of a tap: mask the lanes past K
+                for (int jn = 0; jn < A_INSTR; ++jn)
+                    dy_vo[jn] = k0 + a_k[jn] >= K ? 0x80000000u : dy_vo[jn];
+#pragma unroll
+                for (int jn = 0; jn < B_INSTR; ++jn)
+                    w_vo[jn] = k0 + b_k[jn] >= K ? 0x80000000u : w_vo[jn];
+            }
+            so_a = pin((uint32_t)k0 * 2u);
+            so_b = pin(q_wtap + (uint32_t)(k0 * RSC) * 2u);
+        } else {                  // a z item
+            const int x0 = (item - niter) * LD;
 #pragma unroll
             for (int jn = 0; jn < A_INSTR; ++jn)
-                dy_vo[jn] = k0 + a_k[jn] >= K ? 0x80000000u : dy_vo[jn];
+                dy_vo[jn] = z_offset(x0 + jn);
 #pragma unroll
             for (int jn = 0; jn < B_INSTR; ++jn)
-                w_vo[jn] = k0 + b_k[jn] >= K ? 0x80000000u : w_vo[jn];
-        }
-        q_base = lds_u32 + (uint32_t)(buf * STAGE);
-    };
-    // Issue load number x of the prepared slice (dy blocks first, then
-    // filter blocks).
-    auto issue_one = [&](int x) {
-        if (x < A_INSTR) {
-            dma16(dy_desc, dy_vo[x], (uint32_t)k0 * 2u, q_base + (uint32_t)((x * NW + wave) * 1024));
-        } else {
-            const int jn = x - A_INSTR;
-            dma16(w_desc, w_vo[jn], q_wtap + (uint32_t)(k0 * RSC) * 2u,
-                  q_base + (uint32_t)(A_BYTES + (jn * NW + wave) * 1024));
+                w_vo[jn] = z_offset(x0 + A_INSTR + jn);
+            desc_a = z_desc;
+            desc_b = z_desc;
+            so_a = 0;
+            so_b = 0;
         }
     };
-    auto advance = [&]() {        // the cursor past the issued slice: k innermost, then taps
+    // Issue load X of the prepared item into stage ST.
+    auto issue_one = [&](auto st_c, auto x_c) __attribute__((always_inline)) {
+        constexpr int ST = decltype(st_c)::value;
+        constexpr int X = decltype(x_c)::value;
+        if constexpr (X < A_INSTR)
+            dma16_at<(uint32_t)(ST * STAGE + X * NW * 1024)>(desc_a, dy_vo[X], so_a, dma_base);
+        else
+            dma16_at<(uint32_t)(ST * STAGE + X * NW * 1024)>(desc_b, w_vo[X - A_INSTR], so_b, dma_base);
+    };
+    auto advance = [&]() __attribute__((always_inline)) {        // past the issued item; for a slice: k innermost, then taps
+        ++item;
         k0 += BK;
         if (k0 >= K) {
             k0 = 0;
@@ -200,7 +271,8 @@ dgrad_wide(KernelArgs a)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 acc[fn][fm][e] = 0.0f;
-    auto read_frags = [&](int sb, int kk, half8_t (&af)[FN], half8_t (&bf)[FM]) {
+    auto read_frags = [&](auto st_c, int kk, half8_t (&af)[FN], half8_t (&bf)[FM]) __attribute__((always_inline)) {
+        constexpr int sb = decltype(st_c)::value * STAGE;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const lds_char* p = (lds_char*)lds + sb + a_frag[fn] + kk * 16 * B_ROW;
@@ -223,91 +295,98 @@ dgrad_wide(KernelArgs a)
     //
     // One barrier per slice, in its middle: after the operations of sub-step 2
     // are issued, the wave waits for its loads of slice it + 1 (its loads of
-    // slice it + 2, issued since, may stay in flight) and for its own
+    // item it + 2, issued since, may stay in flight) and for its own
     // fragment reads of slice it, then meets the other waves. Past that
     // barrier (a) slice it + 1 is in LDS and (b) no wave reads slice it's
     // stage any more, so set 0 is refilled with sub-step 0 of slice it + 1
     // while sub-step 3 runs, set 1 with its sub-step 1 after, and slice it +
-    // 1's loads of slice it + 3 may overwrite stage it % 3. The next slice
+    // 1's loads of item it + 3 may overwrite stage it % 3. The next slice
     // then starts on fragments already in registers, and the operations in
     // flight keep the matrix core busy while the wave waits at the barrier.
+    // Every slice has the same instruction stream (the z items stand in for
+    // the missing slices it + 2 at the end), which keeps branches out of it.
     //
-    // The LD loads of slice it + 2 go out one at a time between the
+    // The LD loads of item it + 2 go out one at a time between the
     // operations of sub-steps 0-2 (with one wave per SIMD, a load whose issue
     // waits for the address unit then holds up no operation: the one just
     // issued keeps the matrix core busy). The scheduling barriers keep that
     // order.
     constexpr int OPS = FM * FN;          // operations per sub-step
     half8_t af[2][FN], bf[2][FM];
-    auto ops = [&](int f, int kk, bool issue) {
-#pragma unroll
-        for (int j = 0; j < OPS; ++j) {
-            const int fm = j / FN, fn = j % FN;
+    auto ops = [&](auto st_c, int f, auto kk_c, auto issue_c) __attribute__((always_inline)) {
+        constexpr int KK = decltype(kk_c)::value;
+        static_for<0, OPS>([&](auto j_c) {
+            constexpr int J = decltype(j_c)::value;
+            constexpr int fm = J / FN, fn = J % FN;
             acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[f][fn], bf[f][fm], acc[fn][fm], 0, 0, 0);
-            const int op = kk * OPS + j;
-#pragma unroll
-            for (int x = 0; x < LD; ++x)
-                if (x * 3 * OPS / LD == op && issue)
-                    issue_one(x);
+            if constexpr (decltype(issue_c)::value) {
+                static_for<0, LD>([&](auto x_c) {
+                    if constexpr (decltype(x_c)::value * 3 * OPS / LD == KK * OPS + J)
+                        issue_one(st_c, x_c);
+                });
+            }
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
 
-    prepare(0);
-#pragma unroll
-    for (int x = 0; x < LD; ++x)
-        issue_one(x);
-    advance();
-    if (niter > 1) {
-        prepare(1);
-#pragma unroll
-        for (int x = 0; x < LD; ++x)
-            issue_one(x);
-        advance();
-        wait_vmcnt<LD>();
-    } else {
-        wait_vmcnt<0>();
-    }
-    __syncthreads();                      // slice 0 is in LDS
-    read_frags(0, 0, af[0], bf[0]);
-    read_frags(0, 1, af[1], bf[1]);
-    int cbuf = 0, rbuf = 2;
-    for (int it = 0; it < niter; ++it) {
-        const int sb = cbuf * STAGE;
-        const bool more = it + 2 < niter;   // loads of slice it + 2 go out during this slice
-        if (more)
-            prepare(rbuf);
-        ops(0, 0, more);
-        read_frags(sb, 2, af[0], bf[0]);
-        ops(1, 1, more);
-        read_frags(sb, 3, af[1], bf[1]);
-        ops(0, 2, more);
-        const int nbuf = cbuf == 2 ? 0 : cbuf + 1;
-        if (it + 1 < niter) {
-            if (more)
-                wait_vmcnt<LD>();
-            else
-                wait_vmcnt<0>();
+    // Slice it in stage ST (= it % 3); item it + 2 (a slice or a z item)
+    // goes out during it into stage (ST + 2) % 3.
+    auto slice = [&](auto st_c, int it) __attribute__((always_inline)) {
+        constexpr IC<(decltype(st_c)::value + 1) % 3> next_c{};
+        constexpr IC<(decltype(st_c)::value + 2) % 3> req_c{};
+        prepare();
+        ops(req_c, 0, IC<0>{}, IC<1>{});
+        read_frags(st_c, 2, af[0], bf[0]);
+        ops(req_c, 1, IC<1>{}, IC<1>{});
+        read_frags(st_c, 3, af[1], bf[1]);
+        ops(req_c, 0, IC<2>{}, IC<1>{});
+        const bool has_next = it + 1 < niter;
+        if (has_next) {
+            // slice it + 1's loads went out before item it + 2's, which may
+            // stay in flight
+            wait_vmcnt<LD>();
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __syncthreads();
-            read_frags(nbuf * STAGE, 0, af[0], bf[0]);
+            read_frags(next_c, 0, af[0], bf[0]);
         }
-        ops(1, 3, false);
-        if (it + 1 < niter)
-            read_frags(nbuf * STAGE, 1, af[1], bf[1]);
-        if (more) {
-            advance();
-            rbuf = rbuf == 2 ? 0 : rbuf + 1;
+        ops(req_c, 1, IC<3>{}, IC<0>{});
+        if (has_next)
+            read_frags(next_c, 1, af[1], bf[1]);
+        advance();
+    };
+
+    // items 0 and 1 (slice 1, or the first z item when niter is 1)
+    prepare();
+    static_for<0, LD>([&](auto x_c) { issue_one(IC<0>{}, x_c); });
+    advance();
+    prepare();
+    static_for<0, LD>([&](auto x_c) { issue_one(IC<1>{}, x_c); });
+    advance();
+    wait_vmcnt<LD>();
+    __syncthreads();                      // slice 0 is in LDS
+    read_frags(IC<0>{}, 0, af[0], bf[0]);
+    read_frags(IC<0>{}, 1, af[1], bf[1]);
+    // three slices per pass, so every stage index is a compile-time constant
+    // (one exit, so the accumulators keep their registers through the loop)
+    for (int it = 0; it < niter;) {
+        slice(IC<0>{}, it);
+        ++it;
+        if (it < niter) {
+            slice(IC<1>{}, it);
+            ++it;
         }
-        cbuf = nbuf;
+        if (it < niter) {
+            slice(IC<2>{}, it);
+            ++it;
+        }
     }
 
     // ---- epilogue: acc x g(z) -> fp16 (RNE), staged through the stage of
     // the last slice and stored as whole pixel rows (see dgrad_igemm). The
     // lane holds channels 8*gq + 4*(lane/32) .. +3 of block fn, pixel lane%32
-    // of pixel group fm. No load is in flight: the last slice's wait was for
-    // all of them.
-    const int sdone = cbuf == 0 ? 2 : cbuf - 1;
+    // of pixel group fm. The two z items may still be in flight: every
+    // wave waits for its loads before the barrier that opens the epilogue.
+    const int sdone = (niter - 1) % 3;
     constexpr int CH = TN / 8;            // 16-byte chunks per staged pixel row
     constexpr int EROW = TN * 2;          // bytes per staged pixel row
     constexpr int EBLK = 32 * EROW;       // bytes per wave per pixel group
@@ -315,42 +394,37 @@ dgrad_wide(KernelArgs a)
     constexpr int EST = 32 / PPI;         // store instructions per pixel group
     static_assert(NW * EBLK <= STAGE, "the staging blocks fit in one stage");
     static_assert(CH >= 2 && CH <= 64 && 64 % CH == 0, "whole pixel rows per store");
-    auto pixel_offset = [&](int m) -> uint32_t {   // dx element offset of lattice row m
-        const uint32_t n = fastdiv((uint32_t)m, ph.div_hw);
-        const uint32_t rem = (uint32_t)m - n * ph.div_hw.d;
-        const uint32_t i = fastdiv(rem, ph.div_w);
-        const uint32_t j = rem - i * (uint32_t)ph.Wp;
-        const uint32_t pix = (n * (uint32_t)a.H + (uint32_t)(ph.ph + s * (int)i)) * (uint32_t)a.W
-                             + (uint32_t)(ph.pw + s * (int)j);
-        return pix * (uint32_t)C;
-    };
-    auto epilogue = [&](auto tag) {
+    auto epilogue = [&](auto tag) __attribute__((always_inline)) {
         constexpr int E = decltype(tag)::value;
         const __amdgpu_buffer_rsrc_t e_dx = make_rsrc(a.dx, a.dx_bytes);
-        const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(E != kEpiNone ? a.z : a.dx, a.dx_bytes);
         const int cw = c0 + wn * TN;      // first channel of this wave's block
-        u32x2 zr[FM][FN][4];      // every z of the wave's block, loaded before the first use
-        if constexpr (E != kEpiNone) {
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = m0 + wm * TM + fm * 32 + (lane & 31);
-                const uint32_t pix = pixel_offset(m);
-                const uint32_t m_bad = (uint32_t)(m >= ph.M);
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        const int c = cw + fn * 32 + 8 * gq + 4 * (lane >> 5);
-                        zr[fm][fn][gq] = __builtin_amdgcn_raw_buffer_load_b64(
-                            z_rsrc, out_of_range_if(m_bad | (uint32_t)(c >= C), (pix + (uint32_t)c) * 2u), 0, 0);
-                    }
-            }
-        }
         lds_char* blk = (lds_char*)lds + sdone * STAGE + wave * EBLK;
-        __syncthreads();   // every wave is done reading the stage's operands
+        wait_vmcnt<0>();   // this wave's part of the z tile is in LDS (and no load writes LDS after the end)
+        __syncthreads();   // every wave is done reading the stage's operands, and the z tile is whole
+        const int pw = lane & 31;
+        // z of pixel group fm (the lane's 4 channels of each 8-channel chunk),
+        // read from LDS one group ahead, before the staging writes of the
+        // group in hand, so the reads overlap the arithmetic
+        u32x2 zr[2][FN][4];
+        auto read_z = [&](int fm, u32x2 (&zz)[FN][4]) __attribute__((always_inline)) {
+            const int p = wm * TM + fm * 32 + pw;                  // z row in the tile
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int cz = wn * TN + fn * 32 + 8 * gq;     // first channel of the chunk
+                    zz[fn][gq] = *(const __attribute__((address_space(3))) u32x2*)(
+                        (lds_char*)lds + z_row_lds(p) + ((((cz >> 3) ^ (p % ZCH)) * 16)) + (lane >> 5) * 8);
+                }
+        };
+        if constexpr (E != kEpiNone)
+            read_z(0, zr[0]);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            const int pw = lane & 31;
+            if constexpr (E != kEpiNone) {
+                if (fm + 1 < FM)
+                    read_z(fm + 1, zr[(fm + 1) & 1]);
+            }
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
@@ -360,7 +434,7 @@ dgrad_wide(KernelArgs a)
                     float v2 = acc[fn][fm][4 * gq + 2];
                     float v3 = acc[fn][fm][4 * gq + 3];
                     if constexpr (E != kEpiNone) {
-                        const half4_t zz = __builtin_bit_cast(half4_t, zr[fm][fn][gq]);
+                        const half4_t zz = __builtin_bit_cast(half4_t, zr[fm & 1][fn][gq]);
                         v0 *= epilogue_factor<E>((float)zz[0]);
                         v1 *= epilogue_factor<E>((float)zz[1]);
                         v2 *= epilogue_factor<E>((float)zz[2]);

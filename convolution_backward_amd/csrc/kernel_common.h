@@ -70,6 +70,40 @@ __device__ inline void dma16(i32x4 desc, uint32_t voffset, uint32_t soffset, uin
                  : "memory", "m0");
 }
 
+// The same load with the LDS address formed in m0 from a wave-uniform base
+// plus a compile-time byte offset: one scalar add per load (it sets SCC,
+// hence the clobber).
+template <uint32_t OFF>
+__device__ inline void dma16_at(i32x4 desc, uint32_t voffset, uint32_t soffset, uint32_t lds_base)
+{
+    // every scalar operand taken from the first lane (uniform by construction),
+    // so the compiler holds it in scalar registers whatever it can prove
+    const i32x4 d{__builtin_amdgcn_readfirstlane(desc.x), __builtin_amdgcn_readfirstlane(desc.y),
+                  __builtin_amdgcn_readfirstlane(desc.z), __builtin_amdgcn_readfirstlane(desc.w)};
+    const int so = __builtin_amdgcn_readfirstlane((int)soffset);
+    const int lb = __builtin_amdgcn_readfirstlane((int)lds_base);
+    asm volatile("s_add_u32 m0, %3, %4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voffset), "s"(d), "s"(so), "s"(lb), "n"(OFF)
+                 : "memory", "m0", "scc");
+}
+
+// Compile-time integers as values (IC<N>{}), and a loop over them whose body
+// sees its index as a constant expression (decltype(i)::value).
+template <int N>
+struct IC {
+    static constexpr int value = N;
+};
+
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // A wave-uniform 32-bit value kept in a scalar register: the compiler may
 // not re-derive it later from the kernel arguments (a scalar memory load,
 // whose wait would also drain the LDS reads in flight). The value is taken
@@ -115,9 +149,17 @@ constexpr int kEpiNone = 0;
 constexpr int kEpiDRelu = 1;
 constexpr int kEpiDHardswish = 2;
 
-// g(z) for the fused epilogues, evaluated in fp32 without branches.
+// g(z) for the fused epilogues, evaluated in fp32 without branches, for z
+// converted from fp16 (every caller's z is an fp16 tensor).
 // g = 1 (none); relu'(z) = [z > 0]; hardswish'(z) = 0 below -3, z/3 + 1/2 on
-// the closed interval [-3, 3], 1 above 3 (the division is correctly rounded).
+// the closed interval [-3, 3], 1 above 3, where z/3 is the correctly rounded
+// fp32 quotient. It is formed without a division: q0 = z * RN(1/3), the
+// residual z - 3*q0 (exact in one fused multiply-add), then q0 plus the
+// residual times RN(1/3). For every fp16 z in [-3, 3] this equals the
+// correctly rounded quotient (checked exhaustively on the host); the
+// division sequence it replaces cost about a dozen instructions per value.
+constexpr float kThirdRN = 0x1.555556p-2f;   // RN(1/3) in fp32
+
 template <int E>
 __device__ inline float epilogue_factor(float z)
 {
@@ -125,7 +167,9 @@ __device__ inline float epilogue_factor(float z)
         return 1.0f;
     if constexpr (E == kEpiDRelu)
         return z > 0.0f ? 1.0f : 0.0f;
-    const float mid = z / 3.0f + 0.5f;
+    const float q0 = z * kThirdRN;
+    const float q = __builtin_fmaf(__builtin_fmaf(-3.0f, q0, z), kThirdRN, q0);
+    const float mid = q + 0.5f;
     return z < -3.0f ? 0.0f : (z > 3.0f ? 1.0f : mid);
 }
 
