@@ -591,10 +591,11 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     // registers, leaves the sum in acc, resets the counter and returns true.
     // A share that finds every other share already arrived is the last one
     // without writing its own partial sums (nor arriving).
-    // The workspace lives in uncached device memory and every access to it is
+    // The workspace is the caller's device memory; every access to it is
     // system-scope (sc0 sc1), so neither side needs an L2 writeback or
-    // invalidate: a share's stores have reached memory once its vmcnt drains,
-    // which precedes its arrival on the counter.
+    // invalidate across the XCDs' separate L2 caches: a share's stores have
+    // reached memory once its vmcnt drains, which precedes its arrival on the
+    // counter.
     auto sk_fixup = [&](int tile, const Tile& t, int stage) -> bool {
         constexpr int NQ = FN * FM * 4;   // 16-byte groups of accumulators per thread
         constexpr int QB = NQ < 8 ? NQ : 8;   // groups summed per pass (loads in flight per thread)
