@@ -850,7 +850,7 @@ int resident(void)
 
 #define CBW_CONFIG_ENTRY(BM, BN, WM, WN) \
     {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN, 3 * (BM + BN) * 64 * 2, kHasStreamK<BM, BN, WM, WN>, \
-     kHasPhaseOrder<BM, BN, WM, WN>, false},
+     kHasPhaseOrder<BM, BN, WM, WN>, false, false},
 const TileConfig kConfigs[] = {CBW_TILE_CONFIGS(CBW_CONFIG_ENTRY)};
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs <= 64, "the launcher keeps per-config state for at most 64 configs");
@@ -889,10 +889,24 @@ const ResidentFn kPrivate[] = {CBW_TILE_CONFIGS(CBW_PRIVATE_ENTRY)};
 
 }  // namespace
 
-// Configuration ids: dgrad_igemm's first, then dgrad_wide's.
-int num_tile_configs() { return kNumConfigs + wide_num_configs(); }
+// Configuration ids: dgrad_igemm's first, then dgrad_wide's, then dgrad_halo's.
+int num_tile_configs() { return kNumConfigs + wide_num_configs() + halo_num_configs(); }
 
-const TileConfig& tile_config(int id) { return id < kNumConfigs ? kConfigs[id] : wide_config(id - kNumConfigs); }
+const TileConfig& tile_config(int id)
+{
+    if (id < kNumConfigs)
+        return kConfigs[id];
+    if (id < kNumConfigs + wide_num_configs())
+        return wide_config(id - kNumConfigs);
+    return halo_config(id - kNumConfigs - wide_num_configs());
+}
+
+bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W, int P, int Q)
+{
+    if (id < kNumConfigs + wide_num_configs())
+        return true;
+    return halo_admits(id - kNumConfigs - wide_num_configs(), R, S, stride, pad, H, W, P, Q);
+}
 
 int plain_fallback(int id)
 {
@@ -910,14 +924,18 @@ int blocks_per_cu(int id)
 {
     if (id >= 0 && id < kNumConfigs)
         return kResident[id]();
-    return wide_blocks_per_cu(id - kNumConfigs);
+    if (id < kNumConfigs + wide_num_configs())
+        return wide_blocks_per_cu(id - kNumConfigs);
+    return halo_blocks_per_cu(id - kNumConfigs - wide_num_configs());
 }
 
 int kernel_private_bytes(int id)
 {
     if (id >= 0 && id < kNumConfigs)
         return kPrivate[id]();
-    return wide_private_bytes(id - kNumConfigs);
+    if (id < kNumConfigs + wide_num_configs())
+        return wide_private_bytes(id - kNumConfigs);
+    return halo_private_bytes(id - kNumConfigs - wide_num_configs());
 }
 
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream)
@@ -926,7 +944,9 @@ hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream)
         return hipErrorInvalidValue;
     if (id < kNumConfigs)
         return kLaunch[id](a, stream);
-    return launch_wide(id - kNumConfigs, a, stream);
+    if (id < kNumConfigs + wide_num_configs())
+        return launch_wide(id - kNumConfigs, a, stream);
+    return launch_halo(id - kNumConfigs - wide_num_configs(), a, stream);
 }
 
 // ============================================================ zero fill

@@ -505,7 +505,7 @@ int wide_private(void)
     X(256, 128, 2, 2)
 
 #define CBW_WIDE_ENTRY(BM, BN, WM, WN) \
-    {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN "w", 3 * (BM + BN) * 64 * 2, false, false, true},
+    {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN "w", 3 * (BM + BN) * 64 * 2, false, false, true, false},
 const TileConfig kWideConfigs[] = {CBW_WIDE_CONFIGS(CBW_WIDE_ENTRY)};
 constexpr int kNumWide = sizeof(kWideConfigs) / sizeof(kWideConfigs[0]);
 

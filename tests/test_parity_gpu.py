@@ -100,6 +100,52 @@ def test_wide_kernel_every_epilogue(shape, epi):
         assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} epi {epi} config {cid}")
 
 
+def _halo_configs():
+    return [cid for cid in range(cb.conv2d_dgrad_num_configs()) if cb.conv2d_dgrad_config_name(cid).endswith("h")]
+
+
+# Stride-1 layers with P = H and Q = W and a filter of at least 3x3 (the halo
+# kernel runs them itself): ragged M, C and K, a K below one chunk, a pixel
+# tile past the end, a single pixel whose taps all but one leave the image,
+# 5x5 and 7x7 filters, and the widest halo the kernel's buffers hold
+# (W = 79 with pad 1: 256 + 2*80 rows).
+HALO_SHAPES = [
+    (2, 15, 13, 136, 72, 3, 3, 1, 1),
+    (4, 28, 28, 192, 320, 3, 3, 1, 1),
+    (3, 7, 7, 512, 136, 3, 3, 1, 1),
+    (1, 5, 5, 8, 8, 7, 7, 1, 3),
+    (2, 10, 10, 16, 40, 5, 5, 1, 2),
+    (1, 6, 79, 24, 24, 3, 3, 1, 1),
+    (1, 1, 1, 8, 8, 3, 3, 1, 1),
+    (2, 3, 40, 264, 200, 3, 3, 1, 1),
+]
+
+
+@pytest.mark.parametrize("epi", [EPI_NONE, EPI_DRELU, EPI_DHARDSWISH])
+@pytest.mark.parametrize("shape", HALO_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_halo_kernel_every_epilogue(shape, epi):
+    cfg = _cfg(shape, epi, seed=11)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in _halo_configs():
+        note(f"halo kernel {shape} epilogue {epi} config {cid}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} epi {epi} config {cid}")
+
+
+@pytest.mark.parametrize("shape", [(2, 15, 13, 136, 72, 3, 3, 1, 1), (1, 6, 79, 24, 24, 3, 3, 1, 1)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_halo_kernel_integer_bit_exact(shape):
+    """Integer inputs (every product and partial sum exact in fp32): the
+    halo kernel's output equals the rounded oracle bit for bit, so no tap
+    reads a wrong row, a stale halo buffer or a nonzero padding row."""
+    cfg = _cfg(shape, EPI_NONE, seed=12)
+    inp = integer_inputs(cfg, lo=-3, hi=3, seed=13)
+    ref16 = oracle.round_to_half(ref_full(cfg, inp))
+    for cid in _halo_configs():
+        note(f"halo kernel integer {shape} config {cid}")
+        _bits_equal(run(cfg, inp, config_id=cid), ref16)
+
+
 # ---------------------------------------------------------------- full sizes
 
 @pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
@@ -166,7 +212,7 @@ def test_fused_layer_streamk_forced_bit_exact():
     try:
         for cid in range(cb.conv2d_dgrad_num_configs()):
             name = cb.conv2d_dgrad_config_name(cid)
-            if name == "256x64x64/4x1" or name.endswith("w"):
+            if name == "256x64x64/4x1" or name.endswith(("w", "h")):
                 continue   # no stream-K variant
             before = cb.conv2d_dgrad_streamk_launches()
             note(f"fused layer, stream-K forced, config {cid} {name}")
