@@ -104,18 +104,20 @@ def _halo_configs():
     return [cid for cid in range(cb.conv2d_dgrad_num_configs()) if cb.conv2d_dgrad_config_name(cid).endswith("h")]
 
 
-# Stride-1 layers with P = H and Q = W and a filter of at least 3x3 (the halo
-# kernel runs them itself): ragged M, C and K, a K below one chunk, a pixel
-# tile past the end, a single pixel whose taps all but one leave the image,
-# 5x5 and 7x7 filters, and the widest halo the kernel's buffers hold
-# (W = 79 with pad 1: 256 + 2*80 rows).
+# 3x3 stride-1 layers with pad 1 (P = H, Q = W; the halo kernel runs them
+# itself): ragged M, C and K; one k chunk (K <= 64, and K = 64 exactly), two,
+# three, four and five chunks (the chunk walk pairs chunks after one alone
+# when their count before the last is odd); a pixel tile past the end; a
+# single pixel, whose taps all but one leave the image; and the widest halo
+# the buffers hold (W = 67: 256 + 2*68 rows).
 HALO_SHAPES = [
     (2, 15, 13, 136, 72, 3, 3, 1, 1),
     (4, 28, 28, 192, 320, 3, 3, 1, 1),
     (3, 7, 7, 512, 136, 3, 3, 1, 1),
-    (1, 5, 5, 8, 8, 7, 7, 1, 3),
-    (2, 10, 10, 16, 40, 5, 5, 1, 2),
-    (1, 6, 79, 24, 24, 3, 3, 1, 1),
+    (2, 10, 10, 16, 40, 3, 3, 1, 1),
+    (1, 5, 5, 8, 64, 3, 3, 1, 1),
+    (1, 9, 9, 64, 128, 3, 3, 1, 1),
+    (1, 6, 67, 24, 24, 3, 3, 1, 1),
     (1, 1, 1, 8, 8, 3, 3, 1, 1),
     (2, 3, 40, 264, 200, 3, 3, 1, 1),
 ]
@@ -132,7 +134,8 @@ def test_halo_kernel_every_epilogue(shape, epi):
         assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} epi {epi} config {cid}")
 
 
-@pytest.mark.parametrize("shape", [(2, 15, 13, 136, 72, 3, 3, 1, 1), (1, 6, 79, 24, 24, 3, 3, 1, 1)],
+@pytest.mark.parametrize("shape", [(2, 15, 13, 136, 72, 3, 3, 1, 1), (1, 6, 67, 24, 24, 3, 3, 1, 1),
+                                   (2, 3, 40, 264, 200, 3, 3, 1, 1)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_halo_kernel_integer_bit_exact(shape):
     """Integer inputs (every product and partial sum exact in fp32): the
