@@ -61,7 +61,7 @@ def roofline_of(cfg, seconds):
             "frac": achieved / HBM_PEAK_GBS}
 
 
-KERNEL_SOURCES = ("dgrad_kernels.hip", "dgrad_wide.hip", "dgrad_halo.hip", "kernel_common.h", "dgrad_internal.h")
+KERNEL_SOURCES = ("dgrad_kernels.hip", "dgrad_wide.hip", "dgrad_halo.hip", "dgrad_pgemm.hip", "kernel_common.h", "dgrad_internal.h")
 
 
 def kernel_source_digest():

@@ -121,8 +121,8 @@ struct TileConfig {
     bool phase_order;    // supports tile order 2 (phases of a pixel block side by side)
     bool plain_only;     // runs launches of GEMM tiles only, one tile per workgroup (dgrad_wide,
                          // dgrad_halo); the host gives launches with zero phases to plain_fallback(id)
-    bool halo_only;      // runs only the layers tile_config_admits() accepts (dgrad_halo); the host
-                         // gives other layers to plain_fallback(id)
+    bool restricted;     // runs only the layers tile_config_admits() accepts (dgrad_halo, dgrad_pgemm);
+                         // the host gives other layers to plain_fallback(id)
 };
 
 // ------------------------------------------------------------------ wgrad
@@ -241,12 +241,21 @@ hipError_t launch_halo(int i, const KernelArgs& a, hipStream_t stream);
 int halo_blocks_per_cu(int i);
 int halo_private_bytes(int i);
 
+// The configurations of dgrad_pgemm (dgrad_pgemm.hip), numbered after those of
+// dgrad_halo.
+int pgemm_num_configs();
+const TileConfig& pgemm_config(int i);
+bool pgemm_admits(int i, int R, int S, int stride, int pad, int K, int epi);
+hipError_t launch_pgemm(int i, const KernelArgs& a, hipStream_t stream);
+int pgemm_blocks_per_cu(int i);
+int pgemm_private_bytes(int i);
+
 int num_tile_configs();
 const TileConfig& tile_config(int id);
-// Whether config `id` runs the layer itself (true for all but halo_only configs
-// outside their layers).
-bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W, int P, int Q);
-int plain_fallback(int id);   // for a plain_only config: the dgrad_igemm config of the same tile
+// Whether config `id` runs the layer itself (true for all but restricted
+// configs outside their layers).
+bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W, int P, int Q, int K, int epi);
+int plain_fallback(int id);   // for a plain_only or restricted config: the dgrad_igemm config of the same tile
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);
 int blocks_per_cu(int id);   // resident workgroups per CU (current device)
 int kernel_private_bytes(int id);   // scratch bytes per lane of a config's kernel (-1: unknown)

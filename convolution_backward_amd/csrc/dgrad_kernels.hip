@@ -889,29 +889,52 @@ const ResidentFn kPrivate[] = {CBW_TILE_CONFIGS(CBW_PRIVATE_ENTRY)};
 
 }  // namespace
 
-// Configuration ids: dgrad_igemm's first, then dgrad_wide's, then dgrad_halo's.
-int num_tile_configs() { return kNumConfigs + wide_num_configs() + halo_num_configs(); }
+// Configuration ids: dgrad_igemm's first, then dgrad_wide's, dgrad_halo's and
+// dgrad_pgemm's. `kind` returns which table id falls in, and the index there.
+namespace {
+int kind(int id, int& i)
+{
+    i = id;
+    if (i < kNumConfigs)
+        return 0;
+    i -= kNumConfigs;
+    if (i < wide_num_configs())
+        return 1;
+    i -= wide_num_configs();
+    if (i < halo_num_configs())
+        return 2;
+    i -= halo_num_configs();
+    return 3;
+}
+}  // namespace
+
+int num_tile_configs() { return kNumConfigs + wide_num_configs() + halo_num_configs() + pgemm_num_configs(); }
 
 const TileConfig& tile_config(int id)
 {
-    if (id < kNumConfigs)
-        return kConfigs[id];
-    if (id < kNumConfigs + wide_num_configs())
-        return wide_config(id - kNumConfigs);
-    return halo_config(id - kNumConfigs - wide_num_configs());
+    int i = 0;
+    switch (kind(id, i)) {
+    case 0: return kConfigs[i];
+    case 1: return wide_config(i);
+    case 2: return halo_config(i);
+    default: return pgemm_config(i);
+    }
 }
 
-bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W, int P, int Q)
+bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W, int P, int Q, int K, int epi)
 {
-    if (id < kNumConfigs + wide_num_configs())
-        return true;
-    return halo_admits(id - kNumConfigs - wide_num_configs(), R, S, stride, pad, H, W, P, Q);
+    int i = 0;
+    switch (kind(id, i)) {
+    case 2: return halo_admits(i, R, S, stride, pad, H, W, P, Q);
+    case 3: return pgemm_admits(i, R, S, stride, pad, K, epi);
+    default: return true;
+    }
 }
 
 int plain_fallback(int id)
 {
     const TileConfig& tc = tile_config(id);
-    if (!tc.plain_only)
+    if (!tc.plain_only && !tc.restricted)
         return id;
     int best = 0;
     for (int i = 0; i < kNumConfigs; ++i)
@@ -922,31 +945,37 @@ int plain_fallback(int id)
 
 int blocks_per_cu(int id)
 {
-    if (id >= 0 && id < kNumConfigs)
-        return kResident[id]();
-    if (id < kNumConfigs + wide_num_configs())
-        return wide_blocks_per_cu(id - kNumConfigs);
-    return halo_blocks_per_cu(id - kNumConfigs - wide_num_configs());
+    int i = 0;
+    switch (kind(id, i)) {
+    case 0: return id >= 0 ? kResident[i]() : 1;
+    case 1: return wide_blocks_per_cu(i);
+    case 2: return halo_blocks_per_cu(i);
+    default: return pgemm_blocks_per_cu(i);
+    }
 }
 
 int kernel_private_bytes(int id)
 {
-    if (id >= 0 && id < kNumConfigs)
-        return kPrivate[id]();
-    if (id < kNumConfigs + wide_num_configs())
-        return wide_private_bytes(id - kNumConfigs);
-    return halo_private_bytes(id - kNumConfigs - wide_num_configs());
+    int i = 0;
+    switch (kind(id, i)) {
+    case 0: return id >= 0 ? kPrivate[i]() : -1;
+    case 1: return wide_private_bytes(i);
+    case 2: return halo_private_bytes(i);
+    default: return pgemm_private_bytes(i);
+    }
 }
 
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream)
 {
     if (id < 0 || id >= num_tile_configs())
         return hipErrorInvalidValue;
-    if (id < kNumConfigs)
-        return kLaunch[id](a, stream);
-    if (id < kNumConfigs + wide_num_configs())
-        return launch_wide(id - kNumConfigs, a, stream);
-    return launch_halo(id - kNumConfigs - wide_num_configs(), a, stream);
+    int i = 0;
+    switch (kind(id, i)) {
+    case 0: return kLaunch[i](a, stream);
+    case 1: return launch_wide(i, a, stream);
+    case 2: return launch_halo(i, a, stream);
+    default: return launch_pgemm(i, a, stream);
+    }
 }
 
 // ============================================================ zero fill

@@ -149,6 +149,71 @@ def test_halo_kernel_integer_bit_exact(shape):
         _bits_equal(run(cfg, inp, config_id=cid), ref16)
 
 
+def _pgemm_configs():
+    return [cid for cid in range(cb.conv2d_dgrad_num_configs()) if cb.conv2d_dgrad_config_name(cid).endswith("p")]
+
+
+# The persistent GEMM kernel (1x1, stride 1, no padding, K a multiple of 64):
+# ragged M and C; 1, 4, 5 and 8 k steps; one tile per workgroup, and one to
+# two and three to four tiles per workgroup (the slice requests cross tile
+# boundaries, the first slice after an epilogue lets its stores stay in
+# flight). The full-size 1x1 layer of the every-config tests walks six to
+# seven.
+PGEMM_SHAPES = [
+    (2, 15, 13, 136, 256, 1, 1, 1, 0),
+    (1, 7, 9, 64, 512, 1, 1, 1, 0),
+    (3, 9, 11, 200, 64, 1, 1, 1, 0),
+    (4, 28, 28, 192, 320, 1, 1, 1, 0),
+    (32, 28, 28, 512, 64, 1, 1, 1, 0),
+    (256, 14, 14, 512, 256, 1, 1, 1, 0),
+    (128, 14, 14, 1024, 256, 1, 1, 1, 0),
+]
+
+
+@pytest.mark.parametrize("shape", PGEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_pgemm_kernel(shape):
+    cfg = _cfg(shape, EPI_NONE, seed=14)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in _pgemm_configs():
+        note(f"persistent GEMM kernel {shape} config {cid}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} config {cid}")
+
+
+@pytest.mark.parametrize("shape", [(4, 28, 28, 192, 320, 1, 1, 1, 0), (32, 28, 28, 512, 64, 1, 1, 1, 0),
+                                   (256, 14, 14, 512, 256, 1, 1, 1, 0)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_pgemm_kernel_integer_bit_exact(shape):
+    """Integer inputs: the persistent GEMM kernel's output equals the rounded
+    oracle bit for bit, two calls in a row (every tile of every round)."""
+    cfg = _cfg(shape, EPI_NONE, seed=15)
+    inp = integer_inputs(cfg, lo=-3, hi=3, seed=16)
+    ref16 = oracle.round_to_half(ref_full(cfg, inp))
+    for cid in _pgemm_configs():
+        note(f"persistent GEMM kernel integer {shape} config {cid}")
+        _bits_equal(run(cfg, inp, config_id=cid, repeat=2), ref16)
+
+
+# Layers outside the GEMM kernel's class, asked for by its config id: the
+# host runs the plain kernel of the same tile (a 3x3 stride-2 layer, a 1x1
+# stride-2 layer with zero phases, a 1x1 layer with padding, K not a multiple
+# of 64, fused epilogue factors).
+@pytest.mark.parametrize("shape,epi", [((4, 28, 28, 96, 128, 3, 3, 2, 1), EPI_NONE),
+                                       ((8, 28, 28, 128, 256, 1, 1, 2, 0), EPI_NONE),
+                                       ((2, 9, 9, 64, 128, 1, 1, 1, 1), EPI_NONE),
+                                       ((3, 9, 11, 200, 72, 1, 1, 1, 0), EPI_NONE),
+                                       ((2, 15, 13, 136, 256, 1, 1, 1, 0), EPI_DRELU),
+                                       ((2, 15, 13, 136, 256, 1, 1, 1, 0), EPI_DHARDSWISH)],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_pgemm_config_outside_its_layers(shape, epi):
+    cfg = _cfg(shape, epi, seed=17)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in _pgemm_configs():
+        note(f"persistent GEMM config {cid} on {shape} epilogue {epi}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} epi {epi} config {cid}")
+
+
 # ---------------------------------------------------------------- full sizes
 
 @pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
@@ -215,7 +280,7 @@ def test_fused_layer_streamk_forced_bit_exact():
     try:
         for cid in range(cb.conv2d_dgrad_num_configs()):
             name = cb.conv2d_dgrad_config_name(cid)
-            if name == "256x64x64/4x1" or name.endswith(("w", "h")):
+            if name == "256x64x64/4x1" or name.endswith(("w", "h", "p")):
                 continue   # no stream-K variant
             before = cb.conv2d_dgrad_streamk_launches()
             note(f"fused layer, stream-K forced, config {cid} {name}")
