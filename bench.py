@@ -74,9 +74,10 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key):
+def measured_traffic(kernel_key, tile_config):
     """HBM bytes per launch from the committed rocprofv3 counter summary, when
-    it was taken on the current kernel source; else None."""
+    it was taken on the current kernel source with the same tile config; else
+    None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -84,8 +85,14 @@ def measured_traffic(kernel_key):
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_digest():
         return None
-    entry = t.get("layers", {}).get(kernel_key)
-    return None if entry is None else entry.get("bytes_per_launch")
+    return t.get("by_tile_config", {}).get(kernel_key, {}).get(tile_config)
+
+
+def kernel_of(tile_config):
+    """The kernel template a tile-config name runs (its suffix, stream-K aside)."""
+    base = tile_config.split("+")[0]
+    kind = {"w": "dgrad_wide", "h": "dgrad_halo", "p": "dgrad_pgemm"}.get(base[-1], "dgrad_igemm")
+    return f"{kind}<{base}>"
 
 
 def cpu_model():
@@ -496,10 +503,10 @@ def main():
     dom = max(range(len(layers)), key=lambda i: per_layer[i]["avg_us"])
     dcfg = layers[dom][0]
     roof = roofline_of(dcfg, per_layer[dom]["avg_us"] * 1e-6)
-    roof["kernel"] = f"dgrad_igemm<{per_layer[dom]['tile_config']}> on {dcfg.name}"
+    roof["kernel"] = f"{kernel_of(per_layer[dom]['tile_config'])} on {dcfg.name}"
     roof["unit_of_work"] = ("one layer call = one launch; algorithmic bytes dy + w + dx (+ z), each once, "
                             f"{dcfg.algorithmic_bytes()} B; cold mean of {args.steps} launches")
-    roof["traffic"] = measured_traffic(dcfg.name)
+    roof["traffic"] = measured_traffic(dcfg.name, per_layer[dom]["tile_config"])
     roof["kernel_source_sha256_16"] = kernel_source_digest()
 
     cpu = None
