@@ -172,6 +172,9 @@ def main():
                     help="timed calls of the fused two-step chain and of the unfused pair, after the rest (0 skips)")
     ap.add_argument("--only", default="",
                     help="comma-separated layer names: time only these (for profiler runs)")
+    ap.add_argument("--flush", choices=("write", "read"), default="write",
+                    help="how the cold mode evicts the caches before each layer call: a 512 MiB write "
+                         "(the protocol's cache-flush write) or a 512 MiB read")
     ap.add_argument("--copy-calibrate-mb", type=float, default=0.0,
                     help="run only a plain device-to-device copy of this many MB, 10 times "
                          "(reference for the HBM byte counters) and exit")
@@ -237,17 +240,18 @@ def main():
             one_layer(cfg, d)
     torch.cuda.synchronize()
 
-    # ---- timed steps, cold: before each layer call a 512 MiB read evicts L2
-    # (4 MiB per XCD) and the 256 MiB Infinity Cache; the event pair on the
-    # launch stream brackets the layer call alone
+    # ---- timed steps, cold: before each layer call a 512 MiB write (or read,
+    # --flush read) evicts L2 (4 MiB per XCD) and the 256 MiB Infinity Cache;
+    # the event pair on the launch stream brackets the layer call alone
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    evict = (lambda: flush.fill_(0.0)) if args.flush == "write" else (lambda: flush.sum())
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in layers] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         for li, (cfg, d) in enumerate(layers):
-            flush.sum()
+            evict()
             ev[s][li][0].record(stream)
             one_layer(cfg, d)
             ev[s][li][1].record(stream)
@@ -277,6 +281,32 @@ def main():
         })
         log(f"[cold] {cfg.name:34s} {avg*1e3:9.2f} us  {per_layer[-1]['tflops']:7.1f} TFLOP/s  "
             f"{per_layer[-1]['alg_gbs']:7.0f} GB/s  {rl['bound']} {rl['frac']:.1%}  [{per_layer[-1]['tile_config']}]")
+
+    # ---- the same cold loop with the other eviction (context, not `value`):
+    # a write leaves dirty lines in the Infinity Cache whose write-back lands
+    # inside the timed call, a read does not
+    flops_total = sum(cfg.useful_flops() for cfg, _ in layers)
+    other = "read" if args.flush == "write" else "write"
+    evict2 = (lambda: flush.fill_(0.0)) if other == "write" else (lambda: flush.sum())
+    ev2 = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in layers] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        for li, (cfg, d) in enumerate(layers):
+            evict2()
+            ev2[s][li][0].record(stream)
+            one_layer(cfg, d)
+            ev2[s][li][1].record(stream)
+    torch.cuda.synchronize()
+    ms2 = float(np.mean([sum(ev2[s][li][0].elapsed_time(ev2[s][li][1]) for li in range(len(layers)))
+                         for s in range(args.steps)]))
+    other_flush = {"flush": other, "note": f"the cold loop with a 512 MiB {other} before each layer call instead",
+                   "value": flops_total / (ms2 * 1e-3) / 1e12, "ms_per_step": ms2,
+                   "layers": [{"layer": cfg.name,
+                               "avg_us": float(np.mean([ev2[s][li][0].elapsed_time(ev2[s][li][1])
+                                                        for s in range(args.steps)])) * 1e3}
+                              for li, (cfg, d) in enumerate(layers)]}
+    log(f"[cold, {other} flush] " + "  ".join(f"{x['layer'][:18]} {x['avg_us']:.1f}" for x in other_flush["layers"]))
     del flush
 
     # ---- warm: the layers back to back (operands partly in the caches, like
@@ -536,12 +566,13 @@ def main():
             "timing": "cold",
         },
         "mfma_frac_of_peak": value / MFMA_PEAK_TFLOPS,
-        "timing": "cold: each layer call after a 512 MiB read; per-layer HIP events on the launch stream; "
+        "timing": f"cold: each layer call after a 512 MiB {args.flush}; per-layer HIP events on the launch stream; "
                   f"{args.steps} launches per layer; wall time of the timed loop {cold_wall:.3f} s "
                   "(flushes included)",
         "roofline": roof,
         "cpu_baseline": cpu,
         "layers": per_layer,
+        "cold_other_flush": other_flush,
         "warm": warm,
         "e2e": e2e,
         "workspace_bytes": ws_bytes,
