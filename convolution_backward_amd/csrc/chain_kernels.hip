@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void chain_igemm(ChainArgs a)
             const int m = m0 + wm * 32 + row;
             const int ci = ch * kBN2 + wn * 64 + cc * 8;
             const uint32_t bad = (uint32_t)((m >= a.M) | (ci >= a.C));
-            __builtin_amdgcn_raw_buffer_store_b128(v, dx_r, out_of_range_if(bad, ((uint32_t)m * (uint32_t)a.C + (uint32_t)ci) * 2u), 0, kStorePolicy);
+            __builtin_amdgcn_raw_buffer_store_b128(v, dx_r, out_of_range_if(bad, ((uint32_t)m * (uint32_t)a.C + (uint32_t)ci) * 2u), 0, kStoreNT);
         }
     };
     for (int u = 0; u < ns2; ++u) {

@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                              + (uint32_t)zc_pw + (uint32_t)s * j;
         const uint32_t bad = (uint32_t)!valid | (uint32_t)(m >= (uint32_t)zc_M);
         const u32x4 zero{0u, 0u, 0u, 0u};
-        __builtin_amdgcn_raw_buffer_store_b128(zero, dx_rsrc, out_of_range_if(bad, (pix * (uint32_t)C + c) * 2u), 0, kStorePolicy);
+        __builtin_amdgcn_raw_buffer_store_b128(zero, dx_rsrc, out_of_range_if(bad, (pix * (uint32_t)C + c) * 2u), 0, kStoreSystem);
     };
 
     // ---- request side: the stream of slices of this workgroup's GEMM tiles,
@@ -515,6 +515,9 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
     static_assert(NW * EBLK <= STAGE, "the staging blocks fit in one stage");
     static_assert(CH >= 2 && CH <= 64 && 64 % CH == 0, "whole pixel rows per store");
     constexpr int kEpiStores = FM * EST;     // stores of one epilogue (per wave)
+    // launches with zero phases are mostly stores: their dx goes out with the
+    // system-scope policy, the others' with the non-temporal hint
+    constexpr int kEpiPolicy = (MODE == kCompanion || MODE == kZeroWork) ? kStoreSystem : kStoreNT;
     static_assert(LD + 2 * kMaxZeroPerSlice + kEpiStores < 64, "vmcnt range");
     auto epilogue = [&](auto tag, const Tile& t, const PhaseArg& ph, int stage) {
         constexpr int E = decltype(tag)::value;
@@ -575,10 +578,10 @@ __global__ void __launch_bounds__(64 * WM * WN) dgrad_igemm(KernelArgs a)
                 const int c = cw + q * 8;
                 const uint32_t bad = (uint32_t)(m >= ph.M) | (uint32_t)(c >= C);
                 const uint32_t off = (pixel_offset(ph, m) + (uint32_t)c) * 2u;
-                __builtin_amdgcn_raw_buffer_store_b128(v, e_dx, out_of_range_if(bad, off), 0, kStorePolicy);
+                __builtin_amdgcn_raw_buffer_store_b128(v, e_dx, out_of_range_if(bad, off), 0, kEpiPolicy);
                 const u32x4 zero{0u, 0u, 0u, 0u};
                 for (int qc = 0; qc < ncomp; ++qc)   // companion zero pixels (same lattice point)
-                    __builtin_amdgcn_raw_buffer_store_b128(zero, e_dx, out_of_range_if(bad, off + (uint32_t)a.comp_delta[qc] * 2u), 0, kStorePolicy);
+                    __builtin_amdgcn_raw_buffer_store_b128(zero, e_dx, out_of_range_if(bad, off + (uint32_t)a.comp_delta[qc] * 2u), 0, kEpiPolicy);
             }
         }
     };
@@ -1625,7 +1628,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fwd_igemm(FwdArgs a)
                 const int c = cw + q * 8;
                 const uint32_t bad = (uint32_t)(m >= a.npq) | (uint32_t)(c >= K);
                 const uint32_t off = ((uint32_t)m * (uint32_t)K + (uint32_t)c) * 2u;
-                __builtin_amdgcn_raw_buffer_store_b128(v, out == 0 ? z_rsrc : y_rsrc, out_of_range_if(bad, off), 0, kStorePolicy);
+                __builtin_amdgcn_raw_buffer_store_b128(v, out == 0 ? z_rsrc : y_rsrc, out_of_range_if(bad, off), 0, kStoreNT);
             }
         }
     }

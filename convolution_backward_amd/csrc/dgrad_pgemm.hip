@@ -249,7 +249,7 @@ dgrad_pgemm(KernelArgs a)
         for (int e = 0; e < EST; ++e) {
             const bool ok = col_ok & (e_row + e * PPI < lim);
             __builtin_amdgcn_raw_buffer_store_b128(ev[e], e_dx, ok ? e_lane + base + (uint32_t)e * e_step : 0x80000000u,
-                                                   0, kStorePolicy);
+                                                   0, kStoreNT);
         }
     };
 

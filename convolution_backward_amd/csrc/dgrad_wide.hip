@@ -456,7 +456,7 @@ dgrad_wide(KernelArgs a)
                 const int c = cw + q * 8;
                 const uint32_t bad = (uint32_t)(m >= ph.M) | (uint32_t)(c >= C);
                 __builtin_amdgcn_raw_buffer_store_b128(v, e_dx, out_of_range_if(bad, (pixel_offset(m) + (uint32_t)c) * 2u),
-                                                       0, kStorePolicy);
+                                                       0, kStoreNT);
             }
         }
     };

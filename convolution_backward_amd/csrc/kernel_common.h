@@ -27,14 +27,18 @@ typedef __attribute__((address_space(3))) char lds_char;
 // tensor the host admits (all are below 2^31 bytes).
 constexpr int kRawBufferFlags = 0x00020000;
 
-// Cache policy of output stores: sc0 sc1 (system scope), so an output line,
-// written once and never read back by the kernel, goes on towards memory
-// instead of staying dirty in L2. Measured on MI355X per layer, cold: the 1x1
-// stride-2 layer, whose 617 MB are two-thirds stores, 148-149 us against
-// 168-171 us with the non-temporal hint (nt) and 144-149 us with no bits;
-// the 1x1 stride-1 layer 50.5 us against 51.8 (nt) and 53.1-53.7 (none); the
-// other suite layers within noise of both.
-constexpr int kStorePolicy = 17;
+// Cache policies of output stores (an output is written once and never read
+// back by the kernel). kStoreNT, the non-temporal hint, keeps its lines from
+// displacing operand lines in L2. kStoreSystem, sc0 sc1 (system scope), sends
+// them on towards memory instead of leaving them dirty in L2; it is the
+// better one where most of a launch's bytes are stores, as in layers whose
+// zero phases are stored beside the GEMM pixels. Measured on MI355X, cold: the
+// 1x1 stride-2 layer (617 MB, two-thirds stores) 145-149 us with kStoreSystem
+// against 168-171 us with kStoreNT; elsewhere kStoreNT is equal or better
+// (the fused two-step chain 180-198 against 205-216 us, the forward 1x1
+// stride-2 layer 155-159 against 171-172 us).
+constexpr int kStoreNT = 2;
+constexpr int kStoreSystem = 17;
 
 // Byte offset for a buffer access: `off` itself (below 2^31 for an in-range
 // lane), or exactly 2^31 when bad == 1. Arithmetic, not a select, so no branch
