@@ -121,7 +121,8 @@ struct TileConfig {
     bool phase_order;    // supports tile order 2 (phases of a pixel block side by side)
     bool plain_only;     // runs launches of GEMM tiles only, one tile per workgroup (dgrad_wide,
                          // dgrad_halo); the host gives launches with zero phases to plain_fallback(id)
-    bool restricted;     // runs only the layers tile_config_admits() accepts (dgrad_halo, dgrad_pgemm);
+    bool restricted;     // runs only the layers tile_config_admits() accepts (dgrad_halo, dgrad_pgemm,
+                         // dgrad_halo1);
                          // the host gives other layers to plain_fallback(id)
 };
 
@@ -249,6 +250,15 @@ bool pgemm_admits(int i, int R, int S, int stride, int pad, int K, int epi);
 hipError_t launch_pgemm(int i, const KernelArgs& a, hipStream_t stream);
 int pgemm_blocks_per_cu(int i);
 int pgemm_private_bytes(int i);
+
+// The configurations of dgrad_halo1 (dgrad_halo1.hip), numbered after those
+// of dgrad_pgemm.
+int halo1_num_configs();
+const TileConfig& halo1_config(int i);
+bool halo1_admits(int i, int R, int S, int stride, int pad, int H, int W, int P, int Q, int K, int epi);
+hipError_t launch_halo1(int i, const KernelArgs& a, hipStream_t stream);
+int halo1_blocks_per_cu(int i);
+int halo1_private_bytes(int i);
 
 int num_tile_configs();
 const TileConfig& tile_config(int id);

@@ -892,8 +892,9 @@ const ResidentFn kPrivate[] = {CBW_TILE_CONFIGS(CBW_PRIVATE_ENTRY)};
 
 }  // namespace
 
-// Configuration ids: dgrad_igemm's first, then dgrad_wide's, dgrad_halo's and
-// dgrad_pgemm's. `kind` returns which table id falls in, and the index there.
+// Configuration ids: dgrad_igemm's first, then dgrad_wide's, dgrad_halo's,
+// dgrad_pgemm's and dgrad_halo1's. `kind` returns which table id falls in,
+// and the index there.
 namespace {
 int kind(int id, int& i)
 {
@@ -907,11 +908,17 @@ int kind(int id, int& i)
     if (i < halo_num_configs())
         return 2;
     i -= halo_num_configs();
-    return 3;
+    if (i < pgemm_num_configs())
+        return 3;
+    i -= pgemm_num_configs();
+    return 4;
 }
 }  // namespace
 
-int num_tile_configs() { return kNumConfigs + wide_num_configs() + halo_num_configs() + pgemm_num_configs(); }
+int num_tile_configs()
+{
+    return kNumConfigs + wide_num_configs() + halo_num_configs() + pgemm_num_configs() + halo1_num_configs();
+}
 
 const TileConfig& tile_config(int id)
 {
@@ -920,7 +927,8 @@ const TileConfig& tile_config(int id)
     case 0: return kConfigs[i];
     case 1: return wide_config(i);
     case 2: return halo_config(i);
-    default: return pgemm_config(i);
+    case 3: return pgemm_config(i);
+    default: return halo1_config(i);
     }
 }
 
@@ -930,6 +938,7 @@ bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W,
     switch (kind(id, i)) {
     case 2: return halo_admits(i, R, S, stride, pad, H, W, P, Q);
     case 3: return pgemm_admits(i, R, S, stride, pad, K, epi);
+    case 4: return halo1_admits(i, R, S, stride, pad, H, W, P, Q, K, epi);
     default: return true;
     }
 }
@@ -953,7 +962,8 @@ int blocks_per_cu(int id)
     case 0: return id >= 0 ? kResident[i]() : 1;
     case 1: return wide_blocks_per_cu(i);
     case 2: return halo_blocks_per_cu(i);
-    default: return pgemm_blocks_per_cu(i);
+    case 3: return pgemm_blocks_per_cu(i);
+    default: return halo1_blocks_per_cu(i);
     }
 }
 
@@ -964,7 +974,8 @@ int kernel_private_bytes(int id)
     case 0: return id >= 0 ? kPrivate[i]() : -1;
     case 1: return wide_private_bytes(i);
     case 2: return halo_private_bytes(i);
-    default: return pgemm_private_bytes(i);
+    case 3: return pgemm_private_bytes(i);
+    default: return halo1_private_bytes(i);
     }
 }
 
@@ -977,7 +988,8 @@ hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream)
     case 0: return kLaunch[i](a, stream);
     case 1: return launch_wide(i, a, stream);
     case 2: return launch_halo(i, a, stream);
-    default: return launch_pgemm(i, a, stream);
+    case 3: return launch_pgemm(i, a, stream);
+    default: return launch_halo1(i, a, stream);
     }
 }
 

@@ -149,6 +149,71 @@ def test_halo_kernel_integer_bit_exact(shape):
         _bits_equal(run(cfg, inp, config_id=cid), ref16)
 
 
+def _halo1_configs():
+    return [cid for cid in range(cb.conv2d_dgrad_num_configs()) if cb.conv2d_dgrad_config_name(cid).endswith("s")]
+
+
+# The single-chunk halo kernel (3x3, stride 1, pad 1, K <= 64, all loads at
+# once): ragged M, C and K (K of 8, 24, 40 and 64), images down to 1x1 and 5
+# wide, one up to 67 wide (the widest halo the buffer takes at 128 pixels is
+# 103 wide), one and many tiles.
+HALO1_SHAPES = [
+    (2, 15, 13, 136, 40, 3, 3, 1, 1),
+    (4, 28, 28, 64, 64, 3, 3, 1, 1),
+    (3, 7, 7, 72, 64, 3, 3, 1, 1),
+    (2, 10, 10, 16, 24, 3, 3, 1, 1),
+    (1, 5, 5, 8, 8, 3, 3, 1, 1),
+    (1, 6, 67, 24, 64, 3, 3, 1, 1),
+    (1, 1, 1, 8, 8, 3, 3, 1, 1),
+    (2, 3, 103, 200, 56, 3, 3, 1, 1),
+    (8, 56, 56, 64, 64, 3, 3, 1, 1),
+]
+
+
+@pytest.mark.parametrize("shape", HALO1_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_halo1_kernel(shape):
+    cfg = _cfg(shape, EPI_NONE, seed=18)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in _halo1_configs():
+        note(f"single-chunk halo kernel {shape} config {cid}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} config {cid}")
+
+
+@pytest.mark.parametrize("shape", [(2, 15, 13, 136, 40, 3, 3, 1, 1), (1, 6, 67, 24, 64, 3, 3, 1, 1),
+                                   (8, 56, 56, 64, 64, 3, 3, 1, 1)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_halo1_kernel_integer_bit_exact(shape):
+    """Integer inputs: the single-chunk halo kernel's output equals the
+    rounded oracle bit for bit (no tap reads a wrong row, a padding row or
+    channels past K)."""
+    cfg = _cfg(shape, EPI_NONE, seed=19)
+    inp = integer_inputs(cfg, lo=-3, hi=3, seed=20)
+    ref16 = oracle.round_to_half(ref_full(cfg, inp))
+    for cid in _halo1_configs():
+        note(f"single-chunk halo kernel integer {shape} config {cid}")
+        _bits_equal(run(cfg, inp, config_id=cid, repeat=2), ref16)
+
+
+# Layers outside its class, asked for by its config id, run on the plain
+# kernel of the same tile: K above 64, a halo wider than the buffer, stride
+# 2, 5x5, and fused epilogue factors.
+@pytest.mark.parametrize("shape,epi", [((2, 15, 13, 136, 72, 3, 3, 1, 1), EPI_NONE),
+                                       ((1, 4, 150, 64, 64, 3, 3, 1, 1), EPI_NONE),
+                                       ((2, 14, 14, 64, 64, 3, 3, 2, 1), EPI_NONE),
+                                       ((2, 9, 9, 64, 32, 5, 5, 1, 2), EPI_NONE),
+                                       ((2, 15, 13, 136, 40, 3, 3, 1, 1), EPI_DRELU),
+                                       ((2, 15, 13, 136, 40, 3, 3, 1, 1), EPI_DHARDSWISH)],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_halo1_config_outside_its_layers(shape, epi):
+    cfg = _cfg(shape, epi, seed=21)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in _halo1_configs():
+        note(f"single-chunk halo config {cid} on {shape} epilogue {epi}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} epi {epi} config {cid}")
+
+
 def _pgemm_configs():
     return [cid for cid in range(cb.conv2d_dgrad_num_configs()) if cb.conv2d_dgrad_config_name(cid).endswith("p")]
 
@@ -280,7 +345,7 @@ def test_fused_layer_streamk_forced_bit_exact():
     try:
         for cid in range(cb.conv2d_dgrad_num_configs()):
             name = cb.conv2d_dgrad_config_name(cid)
-            if name == "256x64x64/4x1" or name.endswith(("w", "h", "p")):
+            if name == "256x64x64/4x1" or name.endswith(("w", "h", "p", "s")):
                 continue   # no stream-K variant
             before = cb.conv2d_dgrad_streamk_launches()
             note(f"fused layer, stream-K forced, config {cid} {name}")
