@@ -590,6 +590,35 @@ def test_maximum_sizes_bit_exact(name, shape):
     _compare_in_row_chunks(cfg, inp, gpu, bit_exact=True)
 
 
+# The persistent GEMM kernel ("p") and the single-chunk halo kernel ("s"),
+# asked for by config id, on dx tensors just below the 2^30-element limit, so
+# their dx byte offsets reach the top of the 32-bit range: bit-exact on small
+# integers on the first and last pixel rows and a seeded sample between them
+# (the whole 3x3 tensor would keep the oracle busy for minutes), and no
+# element left unwritten.
+MAX_NEW_KERNELS = [("p", (63, 128, 128, 1024, 64, 1, 1, 1, 0)), ("s", (100, 100, 100, 1024, 64, 3, 3, 1, 1))]
+
+
+@pytest.mark.parametrize("suffix,shape", MAX_NEW_KERNELS, ids=[s for s, _ in MAX_NEW_KERNELS])
+def test_new_kernels_at_maximum_offsets(suffix, shape):
+    cfg = small_config(*shape, name=f"max_{suffix}")
+    npix = cfg.N * cfg.H * cfg.W
+    assert npix * cfg.C < 2 ** 30 and npix * cfg.C > 2 ** 29
+    ids = [c for c in range(cb.conv2d_dgrad_num_configs()) if cb.conv2d_dgrad_config_name(c).endswith(suffix)]
+    assert ids
+    inp = _int8_inputs(cfg, seed=23)
+    rng = np.random.Generator(np.random.PCG64(24))
+    rows = np.unique(np.concatenate([np.arange(0, 2048), np.arange(npix - 8192, npix),
+                                     rng.integers(0, npix, size=4096)])).astype(np.int64)
+    ref16 = oracle.round_to_half(ref_rows(cfg, inp, rows))
+    for cid in ids:
+        note(f"maximum offsets, config {cid} {cb.conv2d_dgrad_config_name(cid)} {shape}")
+        gpu = run(cfg, inp, config_id=cid)
+        assert not np.isnan(gpu).any()
+        _bits_equal(gpu.reshape(npix, cfg.C)[rows], ref16)
+        del gpu
+
+
 # ResNet-50 dgrad layers at batch 256 beyond the measured suite (dx channels C,
 # dy channels K): the stage-2/3/4 3x3 convolutions, the stage-4 strided 3x3
 # and a 1x1 expansion, each with one of the epilogues.
