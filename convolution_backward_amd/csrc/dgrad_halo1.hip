@@ -48,7 +48,7 @@ __host__ __device__ constexpr int halo1_rows(int BM, int rows_per_load, int D)
     return (BM + 2 * D + rows_per_load - 1) / rows_per_load * rows_per_load;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool SPLIT>
 __global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 1)))
 dgrad_halo1(KernelArgs a)
 {
@@ -82,8 +82,15 @@ dgrad_halo1(KernelArgs a)
     const int Q = pin(a.Q);
     const int RSC = pin(9 * C);                   // filter elements per k
 
-    // ---- this workgroup's tile (one phase; the grid is the tile count)
-    const int tile = xcd_remap(blockIdx.x, gridDim.x, a.group, a.xcd_mode);
+    // ---- this workgroup's tile and k chunk (one phase; the grid is the tile
+    // count, times the chunk count when the chunks are split: workgroup
+    // chunk*tiles + tile)
+    const int ntile = pin(a.gemm_tiles);
+    const int nchunk = SPLIT ? pin(a.sk_maxseg) : 1;
+    const int bid = SPLIT ? (int)blockIdx.x % ntile : (int)blockIdx.x;
+    const int chunk = SPLIT ? pin((int)blockIdx.x / ntile) : 0;
+    const int tile = xcd_remap(bid, ntile, a.group, a.xcd_mode);
+    const int kc0 = chunk * 64;                   // the chunk's first dy channel
     const PhaseArg& ph = a.ph[0];
     int tm, tn;
     if (a.order != 1) {    // channel tiles of one pixel block are consecutive
@@ -119,13 +126,14 @@ dgrad_halo1(KernelArgs a)
         const int hq = lane / 9;
         const int hr = lane - 9 * hq;
         const uint32_t hoff0 = (uint32_t)(m0 - D + 7 * wave + hq) * (uint32_t)(2 * K) + (uint32_t)(16 * hr);
-        const bool skip = hr == 8 || 8 * hr >= K;
+        const bool skip = hr == 8 || kc0 + 8 * hr >= K;
         const uint32_t vstep = pin((uint32_t)(RPL * 2 * K));
         const uint32_t h_wave = pin(lds_u32 + (uint32_t)(B0 + wave * 63 * 16));
         static_for<0, HL>([&](auto j_c) {
             constexpr int J = decltype(j_c)::value;
             const bool off = skip || J >= HB;
-            dma16_at<(uint32_t)(J * NW * 63 * 16)>(dy_desc, off ? 0x80000000u : hoff0 + (uint32_t)J * vstep, 0u, h_wave);
+            dma16_at<(uint32_t)(J * NW * 63 * 16)>(dy_desc, off ? 0x80000000u : hoff0 + (uint32_t)J * vstep,
+                                                   pin((uint32_t)(2 * kc0)), h_wave);
         });
     }
 
@@ -144,8 +152,8 @@ dgrad_halo1(KernelArgs a)
             const int b = (X * NW + wave) % FB;
             const int k = 8 * b + (lane >> 3);
             const int cc = ((lane & 7) ^ w_swizzle<B_ROW>(k)) * 8;
-            const uint32_t vo = (k >= K || c0 + cc >= C) ? 0x80000000u : (uint32_t)(k * RSC + cc) * 2u;
-            dma16_at<(uint32_t)(X * NW * 1024)>(w_desc, vo, pin((uint32_t)(T * C + c0) * 2u), dma_base);
+            const uint32_t vo = (kc0 + k >= K || c0 + cc >= C) ? 0x80000000u : (uint32_t)(k * RSC + cc) * 2u;
+            dma16_at<(uint32_t)(X * NW * 1024)>(w_desc, vo, pin((uint32_t)(kc0 * RSC + T * C + c0) * 2u), dma_base);
         });
     }
 
@@ -242,6 +250,88 @@ dgrad_halo1(KernelArgs a)
             }
     });
 
+    // ---- split chunks: the partial sums of the tile's chunks meet. As the
+    // stream-K fix-up of dgrad_igemm: workgroup (tile, chunk) leaves its fp32
+    // sums in workspace slot [tile][chunk] (16-byte group q of thread tid at
+    // float offset (q*NT + tid)*4) and arrives on the tile's counter; the
+    // last to arrive (no workgroup waits for another) adds the chunks in
+    // chunk order, its own from registers, resets the counter and runs the
+    // epilogue; the others end here. A workgroup that finds every other
+    // chunk arrived is the last without writing its own sums. Every
+    // workspace access is system-scope (sc0 sc1), so no L2 writeback or
+    // invalidate is needed across the XCDs' caches: a workgroup's sums have
+    // reached memory once its vmcnt drains, which precedes its arrival.
+    if constexpr (SPLIT) {
+        constexpr int NT = 64 * NW;
+        constexpr int NQ = FN * FM * 4;           // 16-byte groups of accumulators per thread
+        constexpr uint32_t kSegBytes = (uint32_t)BM * BN * 4;
+        constexpr int kSys = 17;                  // cache policy sc0 sc1
+        int* const count = a.sk_count + tile;
+        const __amdgpu_buffer_rsrc_t ws =
+            make_rsrc(a.sk_part + (size_t)tile * (size_t)nchunk * (size_t)(BM * BN), (uint32_t)nchunk * kSegBytes);
+        const uint32_t lane_off = (uint32_t)tid * 16u;
+        __attribute__((address_space(3))) int* flag = (__attribute__((address_space(3))) int*)((lds_char*)lds + Z0);
+        __syncthreads();                          // every wave is done reading the zeros
+        if (tid == 0)
+            *flag = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nchunk - 1 ? 1 : 0;
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(*flag) == 0) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int g = (fn * FM + fm) * 4 + q;
+                        const float4_t v{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2], acc[fn][fm][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws,
+                                                               (uint32_t)chunk * kSegBytes + (uint32_t)(g * NT) * 16u + lane_off, 0, kSys);
+                    }
+            wait_vmcnt<0>();                      // this wave's sums are in memory
+            __syncthreads();                      // ... and every wave's; every wave has read the flag
+            if (tid == 0) {
+                const int old = __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *flag = old == nchunk - 1 ? 1 : 0;
+            }
+            __syncthreads();
+            if (__builtin_amdgcn_readfirstlane(*flag) == 0)
+                return;
+        }
+        // chunk by chunk, all NQ groups of a chunk in flight at once
+        float4_t sum[NQ];
+#pragma unroll
+        for (int g = 0; g < NQ; ++g)
+            sum[g] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int sg = 0; sg < nchunk; ++sg) {
+            float4_t v[NQ];
+            if (sg == chunk) {
+#pragma unroll
+                for (int g = 0; g < NQ; ++g) {
+                    const int fn = g / (FM * 4), fm = (g / 4) % FM, q = g % 4;
+                    v[g] = float4_t{acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1], acc[fn][fm][4 * q + 2], acc[fn][fm][4 * q + 3]};
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < NQ; ++g)
+                    v[g] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            ws, (uint32_t)sg * kSegBytes + (uint32_t)(g * NT) * 16u + lane_off, 0, kSys));
+            }
+#pragma unroll
+            for (int g = 0; g < NQ; ++g)
+                sum[g] += v[g];
+        }
+#pragma unroll
+        for (int g = 0; g < NQ; ++g) {
+            const int fn = g / (FM * 4), fm = (g / 4) % FM, q = g % 4;
+            acc[fn][fm][4 * q] = sum[g][0];
+            acc[fn][fm][4 * q + 1] = sum[g][1];
+            acc[fn][fm][4 * q + 2] = sum[g][2];
+            acc[fn][fm][4 * q + 3] = sum[g][3];
+        }
+        if (tid == 0)
+            __hip_atomic_store(count, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     // ---- epilogue: fp32 -> fp16 (RNE), staged through the first filter tap
     // (every wave is done reading the filter after the barrier) and stored
     // as whole pixel rows. With P = H and stride 1, dx pixel m is lattice row
@@ -284,31 +374,50 @@ dgrad_halo1(KernelArgs a)
     }
 }
 
-// The layers this kernel runs: 3x3, stride 1, pad 1, P = H and Q = W, at most
-// 64 dy channels, no fused epilogue factor, and a halo of at most the rows
-// the buffer holds.
+// The layers this kernel runs: 3x3, stride 1, pad 1, P = H and Q = W, no
+// fused epilogue factor, a halo of at most the rows the buffer holds, and at
+// most 64 dy channels, or up to kHalo1MaxChunks chunks of 64 when the chunks
+// are split over workgroups (which needs a workspace; the host runs such a
+// layer on the plain kernel of the same tile without one).
 template <int BM, int BN, int WM, int WN>
 bool halo1_fits(int R, int S, int stride, int pad, int H, int W, int P, int Q, int K, int epi)
 {
     using Sh = Halo1Shape<BM, BN, WM, WN>;
-    if (stride != 1 || R != 3 || S != 3 || pad != 1 || P != H || Q != W || K < 1 || K > 64 || epi != kEpiNone ||
-        Q > Sh::HR)
+    if (stride != 1 || R != 3 || S != 3 || pad != 1 || P != H || Q != W || K < 1 || K > 64 * kHalo1MaxChunks ||
+        epi != kEpiNone || Q > Sh::HR)
         return false;
     return halo1_rows(BM, Sh::RPL, Q + 1) <= Sh::HR;
 }
 
-// The launch must be that one phase (taps from (0, 0), dy offsets of the
-// first tap = 1) in GEMM tiles only, one per workgroup.
+// Whether the planned launch is one this kernel runs: that one phase (taps
+// from (0, 0), dy offsets of the first tap = 1) in GEMM tiles only, one per
+// workgroup, either whole (K <= 64) or split into its k chunks (one
+// workgroup per tile and chunk, partial sums in the workspace).
+template <int BM, int BN, int WM, int WN>
+bool halo1_runs(const KernelArgs& a)
+{
+    const PhaseArg& ph = a.ph[0];
+    if (a.nzphases > 0 || a.ncomp > 0 || a.zstripes > 0 || a.nphases != 1 || a.total_tiles != a.gemm_tiles ||
+        ph.nr != 3 || ph.nt != 3 || ph.r0 != 0 || ph.t0 != 0 || ph.dr0 != 1 || ph.dt0 != 1 || ph.ph != 0 || ph.pw != 0 ||
+        ph.Wp != a.W || ph.div_hw.d != (uint32_t)(a.H * a.W) ||
+        !halo1_fits<BM, BN, WM, WN>(a.R, a.S, a.stride, 1, a.H, a.W, a.P, a.Q, a.K, a.epi))
+        return false;
+    const int chunks = (a.K + 63) / 64;
+    if (!a.sk)
+        return chunks == 1 && a.grid == a.gemm_tiles;
+    return chunks > 1 && a.sk_maxseg == chunks && (int64_t)a.grid == (int64_t)a.gemm_tiles * chunks &&
+           a.sk_part != nullptr && a.sk_count != nullptr;
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t halo1_launch(const KernelArgs& a, hipStream_t stream)
 {
-    const PhaseArg& ph = a.ph[0];
-    if (a.sk || a.nzphases > 0 || a.ncomp > 0 || a.zstripes > 0 || a.nphases != 1 || a.total_tiles != a.gemm_tiles ||
-        a.grid != a.gemm_tiles || ph.nr != 3 || ph.nt != 3 || ph.r0 != 0 || ph.t0 != 0 || ph.dr0 != 1 ||
-        ph.dt0 != 1 || ph.ph != 0 || ph.pw != 0 || ph.Wp != a.W || ph.div_hw.d != (uint32_t)(a.H * a.W) ||
-        !halo1_fits<BM, BN, WM, WN>(a.R, a.S, a.stride, 1, a.H, a.W, a.P, a.Q, a.K, a.epi))
+    if (!halo1_runs<BM, BN, WM, WN>(a))
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dgrad_halo1<BM, BN, WM, WN>), dim3(a.grid), dim3(64 * WM * WN), 0, stream, a);
+    if (a.sk)
+        hipLaunchKernelGGL((dgrad_halo1<BM, BN, WM, WN, true>), dim3(a.grid), dim3(64 * WM * WN), 0, stream, a);
+    else
+        hipLaunchKernelGGL((dgrad_halo1<BM, BN, WM, WN, false>), dim3(a.grid), dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -316,7 +425,7 @@ template <int BM, int BN, int WM, int WN>
 int halo1_resident(void)
 {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(dgrad_halo1<BM, BN, WM, WN>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(dgrad_halo1<BM, BN, WM, WN, false>),
                                                      64 * WM * WN, 0) != hipSuccess) {
         (void)hipGetLastError();
         return 1;
@@ -327,12 +436,17 @@ int halo1_resident(void)
 template <int BM, int BN, int WM, int WN>
 int halo1_private(void)
 {
-    hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(dgrad_halo1<BM, BN, WM, WN>)) != hipSuccess) {
-        (void)hipGetLastError();
-        return -1;
+    int most = 0;
+    for (const void* f : {reinterpret_cast<const void*>(dgrad_halo1<BM, BN, WM, WN, false>),
+                          reinterpret_cast<const void*>(dgrad_halo1<BM, BN, WM, WN, true>)}) {
+        hipFuncAttributes attr;
+        if (hipFuncGetAttributes(&attr, f) != hipSuccess) {
+            (void)hipGetLastError();
+            return -1;
+        }
+        most = (int)attr.localSizeBytes > most ? (int)attr.localSizeBytes : most;
     }
-    return (int)attr.localSizeBytes;
+    return most;
 }
 
 // The compiled configurations of this kernel: (BM, BN, WM, WN).
@@ -340,18 +454,21 @@ int halo1_private(void)
     X(128, 64, 2, 2)
 
 #define CBW_HALO1_ENTRY(BM, BN, WM, WN) \
-    {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN "s", Halo1Shape<BM, BN, WM, WN>::LDS_USED, false, false, true, true},
+    {BM, BN, 64, WM, WN, #BM "x" #BN "x64/" #WM "x" #WN "s", Halo1Shape<BM, BN, WM, WN>::LDS_USED, true, false, true, true, true},
 const TileConfig kHalo1Configs[] = {CBW_HALO1_CONFIGS(CBW_HALO1_ENTRY)};
 constexpr int kNumHalo1 = sizeof(kHalo1Configs) / sizeof(kHalo1Configs[0]);
 
 using Halo1LaunchFn = hipError_t (*)(const KernelArgs&, hipStream_t);
+using Halo1RunsFn = bool (*)(const KernelArgs&);
 using Halo1FitsFn = bool (*)(int, int, int, int, int, int, int, int, int, int);
 #define CBW_HALO1_LAUNCH(BM, BN, WM, WN) &halo1_launch<BM, BN, WM, WN>,
 #define CBW_HALO1_FITS(BM, BN, WM, WN) &halo1_fits<BM, BN, WM, WN>,
+#define CBW_HALO1_RUNS(BM, BN, WM, WN) &halo1_runs<BM, BN, WM, WN>,
 #define CBW_HALO1_RESIDENT(BM, BN, WM, WN) &halo1_resident<BM, BN, WM, WN>,
 #define CBW_HALO1_PRIVATE(BM, BN, WM, WN) &halo1_private<BM, BN, WM, WN>,
 const Halo1LaunchFn kHalo1Launch[] = {CBW_HALO1_CONFIGS(CBW_HALO1_LAUNCH)};
 const Halo1FitsFn kHalo1Fits[] = {CBW_HALO1_CONFIGS(CBW_HALO1_FITS)};
+const Halo1RunsFn kHalo1Runs[] = {CBW_HALO1_CONFIGS(CBW_HALO1_RUNS)};
 int (*const kHalo1Resident[])(void) = {CBW_HALO1_CONFIGS(CBW_HALO1_RESIDENT)};
 int (*const kHalo1Private[])(void) = {CBW_HALO1_CONFIGS(CBW_HALO1_PRIVATE)};
 
@@ -365,6 +482,8 @@ bool halo1_admits(int i, int R, int S, int stride, int pad, int H, int W, int P,
 {
     return i >= 0 && i < kNumHalo1 && kHalo1Fits[i](R, S, stride, pad, H, W, P, Q, K, epi);
 }
+
+bool halo1_runs_launch(int i, const KernelArgs& a) { return i >= 0 && i < kNumHalo1 && kHalo1Runs[i](a); }
 
 hipError_t launch_halo1(int i, const KernelArgs& a, hipStream_t stream)
 {

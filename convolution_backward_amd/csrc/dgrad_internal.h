@@ -122,8 +122,10 @@ struct TileConfig {
     bool plain_only;     // runs launches of GEMM tiles only, one tile per workgroup (dgrad_wide,
                          // dgrad_halo); the host gives launches with zero phases to plain_fallback(id)
     bool restricted;     // runs only the layers tile_config_admits() accepts (dgrad_halo, dgrad_pgemm,
-                         // dgrad_halo1);
-                         // the host gives other layers to plain_fallback(id)
+                         // dgrad_halo1); the host gives other layers to plain_fallback(id)
+    bool chunk_split;    // splits by k chunk, one workgroup per tile and chunk (dgrad_halo1), instead of
+                         // stream-K's equal slice ranges; a launch tile_config_runs() refuses goes to
+                         // plain_fallback(id)
 };
 
 // ------------------------------------------------------------------ wgrad
@@ -256,6 +258,8 @@ int pgemm_private_bytes(int i);
 int halo1_num_configs();
 const TileConfig& halo1_config(int i);
 bool halo1_admits(int i, int R, int S, int stride, int pad, int H, int W, int P, int Q, int K, int epi);
+bool halo1_runs_launch(int i, const KernelArgs& a);
+constexpr int kHalo1MaxChunks = 8;   // k chunks of 64 a split dgrad_halo1 launch may have
 hipError_t launch_halo1(int i, const KernelArgs& a, hipStream_t stream);
 int halo1_blocks_per_cu(int i);
 int halo1_private_bytes(int i);
@@ -265,6 +269,9 @@ const TileConfig& tile_config(int id);
 // Whether config `id` runs the layer itself (true for all but restricted
 // configs outside their layers).
 bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W, int P, int Q, int K, int epi);
+// Whether config `id` runs launch `a` as planned (false only for a
+// dgrad_halo1 launch of more than one k chunk that is not split).
+bool tile_config_runs(int id, const KernelArgs& a);
 int plain_fallback(int id);   // for a plain_only or restricted config: the dgrad_igemm config of the same tile
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);
 int blocks_per_cu(int id);   // resident workgroups per CU (current device)

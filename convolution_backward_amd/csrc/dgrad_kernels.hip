@@ -943,6 +943,12 @@ bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W,
     }
 }
 
+bool tile_config_runs(int id, const KernelArgs& a)
+{
+    int i = 0;
+    return kind(id, i) != 4 || halo1_runs_launch(i, a);
+}
+
 int plain_fallback(int id)
 {
     const TileConfig& tc = tile_config(id);

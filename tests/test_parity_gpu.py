@@ -195,10 +195,50 @@ def test_halo1_kernel_integer_bit_exact(shape):
         _bits_equal(run(cfg, inp, config_id=cid, repeat=2), ref16)
 
 
+# The same kernel with K above 64, split by k chunk: one workgroup per tile
+# and chunk, the partial sums in the workspace, the last chunk to arrive adds
+# them in chunk order. 2, 4 and 8 chunks, a ragged last chunk (8 channels),
+# ragged C and M, the suite's N=1 layer; without a workspace the host runs
+# these layers on the plain kernel of the same tile.
+HALO1_SPLIT_SHAPES = [
+    (1, 14, 14, 256, 256, 3, 3, 1, 1),
+    (2, 15, 13, 136, 200, 3, 3, 1, 1),
+    (1, 7, 7, 512, 512, 3, 3, 1, 1),
+    (3, 9, 11, 72, 128, 3, 3, 1, 1),
+]
+
+
+@pytest.mark.parametrize("shape", HALO1_SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_halo1_split_kernel(shape):
+    cfg = _cfg(shape, EPI_NONE, seed=25)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in _halo1_configs():
+        note(f"split single-chunk halo kernel {shape} config {cid}")
+        before = cb.conv2d_dgrad_streamk_launches()
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} config {cid}")
+        assert cb.conv2d_dgrad_streamk_launches() > before      # the chunks were split
+        note(f"split single-chunk halo config {cid} without a workspace {shape}")
+        assert_close(run(cfg, inp, config_id=cid, workspace=None), ref, f"{shape} config {cid}, no workspace")
+
+
+@pytest.mark.parametrize("shape", [(1, 14, 14, 256, 256, 3, 3, 1, 1), (2, 15, 13, 136, 200, 3, 3, 1, 1)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_halo1_split_kernel_integer_bit_exact(shape):
+    """Integer inputs: the chunk sums meet in a fixed order, so the split
+    kernel's output equals the rounded oracle bit for bit, call after call."""
+    cfg = _cfg(shape, EPI_NONE, seed=26)
+    inp = integer_inputs(cfg, lo=-3, hi=3, seed=27)
+    ref16 = oracle.round_to_half(ref_full(cfg, inp))
+    for cid in _halo1_configs():
+        note(f"split single-chunk halo kernel integer {shape} config {cid}")
+        _bits_equal(run(cfg, inp, config_id=cid, repeat=3), ref16)
+
+
 # Layers outside its class, asked for by its config id, run on the plain
-# kernel of the same tile: K above 64, a halo wider than the buffer, stride
-# 2, 5x5, and fused epilogue factors.
-@pytest.mark.parametrize("shape,epi", [((2, 15, 13, 136, 72, 3, 3, 1, 1), EPI_NONE),
+# kernel of the same tile: K above 512 (more chunks than a split takes), a
+# halo wider than the buffer, stride 2, 5x5, and fused epilogue factors.
+@pytest.mark.parametrize("shape,epi", [((1, 7, 7, 64, 576, 3, 3, 1, 1), EPI_NONE),
                                        ((1, 4, 150, 64, 64, 3, 3, 1, 1), EPI_NONE),
                                        ((2, 14, 14, 64, 64, 3, 3, 2, 1), EPI_NONE),
                                        ((2, 9, 9, 64, 32, 5, 5, 1, 2), EPI_NONE),
