@@ -61,7 +61,7 @@ def roofline_of(cfg, seconds):
             "frac": achieved / HBM_PEAK_GBS}
 
 
-KERNEL_SOURCES = ("dgrad_kernels.hip", "dgrad_wide.hip", "dgrad_halo.hip", "dgrad_pgemm.hip", "dgrad_halo1.hip", "kernel_common.h", "dgrad_internal.h")
+KERNEL_SOURCES = ("dgrad_kernels.hip", "dgrad_wide.hip", "dgrad_halo.hip", "dgrad_pgemm.hip", "dgrad_halo1.hip", "dgrad_pwide.hip", "kernel_common.h", "dgrad_internal.h")
 
 
 def kernel_source_digest():
@@ -91,7 +91,7 @@ def measured_traffic(kernel_key, tile_config):
 def kernel_of(tile_config):
     """The kernel template a tile-config name runs (its suffix, stream-K aside)."""
     base = tile_config.split("+")[0]
-    kind = {"w": "dgrad_wide", "h": "dgrad_halo", "p": "dgrad_pgemm", "s": "dgrad_halo1"}.get(base[-1], "dgrad_igemm")
+    kind = {"w": "dgrad_wide", "h": "dgrad_halo", "p": "dgrad_pgemm", "s": "dgrad_halo1", "q": "dgrad_pwide"}.get(base[-1], "dgrad_igemm")
     return f"{kind}<{base}>"
 
 

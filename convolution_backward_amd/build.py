@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
-SOURCES = ["dgrad_kernels.hip", "dgrad_wide.hip", "dgrad_halo.hip", "dgrad_pgemm.hip", "dgrad_halo1.hip", "chain_kernels.hip", "dgrad_api.cpp", "dgrad_plan.cpp"]
+SOURCES = ["dgrad_kernels.hip", "dgrad_wide.hip", "dgrad_halo.hip", "dgrad_pgemm.hip", "dgrad_halo1.hip", "dgrad_pwide.hip", "chain_kernels.hip", "dgrad_api.cpp", "dgrad_plan.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -122,7 +122,7 @@ struct TileConfig {
     bool plain_only;     // runs launches of GEMM tiles only, one tile per workgroup (dgrad_wide,
                          // dgrad_halo); the host gives launches with zero phases to plain_fallback(id)
     bool restricted;     // runs only the layers tile_config_admits() accepts (dgrad_halo, dgrad_pgemm,
-                         // dgrad_halo1); the host gives other layers to plain_fallback(id)
+                         // dgrad_halo1, dgrad_pwide); the host gives other layers to plain_fallback(id)
     bool chunk_split;    // splits by k chunk, one workgroup per tile and chunk (dgrad_halo1), instead of
                          // stream-K's equal slice ranges; a launch tile_config_runs() refuses goes to
                          // plain_fallback(id)
@@ -264,13 +264,24 @@ hipError_t launch_halo1(int i, const KernelArgs& a, hipStream_t stream);
 int halo1_blocks_per_cu(int i);
 int halo1_private_bytes(int i);
 
+// The configurations of dgrad_pwide (dgrad_pwide.hip), numbered after those
+// of dgrad_halo1.
+int pwide_num_configs();
+const TileConfig& pwide_config(int i);
+bool pwide_admits(int i, int stride, int epi);
+bool pwide_runs_launch(int i, const KernelArgs& a);   // no zero phases, no split
+hipError_t launch_pwide(int i, const KernelArgs& a, hipStream_t stream);
+int pwide_blocks_per_cu(int i);
+int pwide_private_bytes(int i);
+
 int num_tile_configs();
 const TileConfig& tile_config(int id);
 // Whether config `id` runs the layer itself (true for all but restricted
 // configs outside their layers).
 bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W, int P, int Q, int K, int epi);
 // Whether config `id` runs launch `a` as planned (false only for a
-// dgrad_halo1 launch of more than one k chunk that is not split).
+// dgrad_halo1 launch of more than one k chunk that is not split, and a
+// dgrad_pwide launch with zero phases).
 bool tile_config_runs(int id, const KernelArgs& a);
 int plain_fallback(int id);   // for a plain_only or restricted config: the dgrad_igemm config of the same tile
 hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream);

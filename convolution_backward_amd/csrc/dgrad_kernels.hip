@@ -893,8 +893,8 @@ const ResidentFn kPrivate[] = {CBW_TILE_CONFIGS(CBW_PRIVATE_ENTRY)};
 }  // namespace
 
 // Configuration ids: dgrad_igemm's first, then dgrad_wide's, dgrad_halo's,
-// dgrad_pgemm's and dgrad_halo1's. `kind` returns which table id falls in,
-// and the index there.
+// dgrad_pgemm's, dgrad_halo1's and dgrad_pwide's. `kind` returns which table
+// id falls in, and the index there.
 namespace {
 int kind(int id, int& i)
 {
@@ -911,13 +911,17 @@ int kind(int id, int& i)
     if (i < pgemm_num_configs())
         return 3;
     i -= pgemm_num_configs();
-    return 4;
+    if (i < halo1_num_configs())
+        return 4;
+    i -= halo1_num_configs();
+    return 5;
 }
 }  // namespace
 
 int num_tile_configs()
 {
-    return kNumConfigs + wide_num_configs() + halo_num_configs() + pgemm_num_configs() + halo1_num_configs();
+    return kNumConfigs + wide_num_configs() + halo_num_configs() + pgemm_num_configs() + halo1_num_configs() +
+           pwide_num_configs();
 }
 
 const TileConfig& tile_config(int id)
@@ -928,7 +932,8 @@ const TileConfig& tile_config(int id)
     case 1: return wide_config(i);
     case 2: return halo_config(i);
     case 3: return pgemm_config(i);
-    default: return halo1_config(i);
+    case 4: return halo1_config(i);
+    default: return pwide_config(i);
     }
 }
 
@@ -939,6 +944,7 @@ bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W,
     case 2: return halo_admits(i, R, S, stride, pad, H, W, P, Q);
     case 3: return pgemm_admits(i, R, S, stride, pad, K, epi);
     case 4: return halo1_admits(i, R, S, stride, pad, H, W, P, Q, K, epi);
+    case 5: return pwide_admits(i, stride, epi);
     default: return true;
     }
 }
@@ -946,7 +952,8 @@ bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W,
 bool tile_config_runs(int id, const KernelArgs& a)
 {
     int i = 0;
-    return kind(id, i) != 4 || halo1_runs_launch(i, a);
+    const int kd = kind(id, i);
+    return kd == 4 ? halo1_runs_launch(i, a) : kd == 5 ? pwide_runs_launch(i, a) : true;
 }
 
 int plain_fallback(int id)
@@ -969,7 +976,8 @@ int blocks_per_cu(int id)
     case 1: return wide_blocks_per_cu(i);
     case 2: return halo_blocks_per_cu(i);
     case 3: return pgemm_blocks_per_cu(i);
-    default: return halo1_blocks_per_cu(i);
+    case 4: return halo1_blocks_per_cu(i);
+    default: return pwide_blocks_per_cu(i);
     }
 }
 
@@ -981,7 +989,8 @@ int kernel_private_bytes(int id)
     case 1: return wide_private_bytes(i);
     case 2: return halo_private_bytes(i);
     case 3: return pgemm_private_bytes(i);
-    default: return halo1_private_bytes(i);
+    case 4: return halo1_private_bytes(i);
+    default: return pwide_private_bytes(i);
     }
 }
 
@@ -995,7 +1004,8 @@ hipError_t launch_tile_config(int id, const KernelArgs& a, hipStream_t stream)
     case 1: return launch_wide(i, a, stream);
     case 2: return launch_halo(i, a, stream);
     case 3: return launch_pgemm(i, a, stream);
-    default: return launch_halo1(i, a, stream);
+    case 4: return launch_halo1(i, a, stream);
+    default: return launch_pwide(i, a, stream);
     }
 }
 

@@ -50,7 +50,7 @@ def test_config_names():
     names = [cb.conv2d_dgrad_config_name(i) for i in range(n)]
     assert len(set(names)) == n
     for nm in names:
-        assert re.fullmatch(r"\d+x\d+x64/\d+x\d+[whps]?", nm)
+        assert re.fullmatch(r"\d+x\d+x64/\d+x\d+[whpsq]?", nm)
     with pytest.raises(cb.DgradError):
         cb.conv2d_dgrad_config_name(n)
 

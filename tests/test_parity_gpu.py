@@ -319,6 +319,66 @@ def test_pgemm_config_outside_its_layers(shape, epi):
         assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} epi {epi} config {cid}")
 
 
+def _pwide_configs():
+    return [cid for cid in range(cb.conv2d_dgrad_num_configs()) if cb.conv2d_dgrad_config_name(cid).endswith("q")]
+
+
+# The persistent four-wave kernel for strided layers without zero phases: 3x3
+# stride 2 (four phases of 1, 2, 2 and 4 taps in one launch; even sizes take
+# the phase-interleaved order, odd ones the phase-major one), ragged M, C
+# and K, 5x5 stride 3 (phases with taps past the image), 3x3 stride 2 at 392
+# tiles (workgroups walk one or two tiles, the slice requests crossing tile
+# and phase boundaries).
+PWIDE_SHAPES = [
+    (4, 28, 28, 96, 128, 3, 3, 2, 1),
+    (2, 27, 29, 72, 136, 3, 3, 2, 1),
+    (2, 17, 19, 64, 80, 5, 5, 3, 2),
+    (3, 14, 14, 200, 40, 3, 3, 2, 1),
+    (64, 28, 28, 256, 64, 3, 3, 2, 1),
+]
+
+
+@pytest.mark.parametrize("shape", PWIDE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_pwide_kernel(shape):
+    cfg = _cfg(shape, EPI_NONE, seed=14)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in _pwide_configs():
+        note(f"persistent wide kernel {shape} config {cid}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} config {cid}")
+
+
+@pytest.mark.parametrize("shape", [(64, 28, 28, 256, 64, 3, 3, 2, 1), (2, 27, 29, 72, 136, 3, 3, 2, 1)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_pwide_kernel_integer_bit_exact(shape):
+    """Integer inputs: the persistent four-wave kernel's output equals the
+    rounded oracle bit for bit, two calls in a row (every tile of every
+    phase)."""
+    cfg = _cfg(shape, EPI_NONE, seed=15)
+    inp = integer_inputs(cfg, lo=-3, hi=3, seed=16)
+    ref16 = oracle.round_to_half(ref_full(cfg, inp))
+    for cid in _pwide_configs():
+        note(f"persistent wide kernel integer {shape} config {cid}")
+        _bits_equal(run(cfg, inp, config_id=cid, repeat=2), ref16)
+
+
+# Layers outside its class, asked for by its config id, run on the plain
+# kernel of the same tile: stride 1, a strided layer with zero phases (1x1
+# stride 2), and fused epilogue factors.
+@pytest.mark.parametrize("shape,epi", [((2, 14, 14, 128, 96, 3, 3, 1, 1), EPI_NONE),
+                                       ((8, 28, 28, 128, 256, 1, 1, 2, 0), EPI_NONE),
+                                       ((4, 28, 28, 96, 128, 3, 3, 2, 1), EPI_DRELU),
+                                       ((4, 28, 28, 96, 128, 3, 3, 2, 1), EPI_DHARDSWISH)],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_pwide_config_outside_its_layers(shape, epi):
+    cfg = _cfg(shape, epi, seed=17)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in _pwide_configs():
+        note(f"persistent wide config {cid} on {shape} epilogue {epi}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} epi {epi} config {cid}")
+
+
 # ---------------------------------------------------------------- full sizes
 
 @pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
@@ -385,7 +445,7 @@ def test_fused_layer_streamk_forced_bit_exact():
     try:
         for cid in range(cb.conv2d_dgrad_num_configs()):
             name = cb.conv2d_dgrad_config_name(cid)
-            if name == "256x64x64/4x1" or name.endswith(("w", "h", "p", "s")):
+            if name == "256x64x64/4x1" or name.endswith(("w", "h", "p", "s", "q")):
                 continue   # no stream-K variant
             before = cb.conv2d_dgrad_streamk_launches()
             note(f"fused layer, stream-K forced, config {cid} {name}")

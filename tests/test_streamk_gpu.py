@@ -32,10 +32,10 @@ SHAPES = [
 
 def _streamk_configs():
     """Configurations with a split variant: all but 256x64/4x1 and the
-    kernels without a split ("w", "h", "p", "s")."""
+    kernels without stream-K ("w", "h", "p", "s", "q")."""
     return [cid for cid in range(cb.conv2d_dgrad_num_configs())
             if cb.conv2d_dgrad_config_name(cid) != "256x64x64/4x1"
-            and not cb.conv2d_dgrad_config_name(cid).endswith(("w", "h", "p", "s"))]
+            and not cb.conv2d_dgrad_config_name(cid).endswith(("w", "h", "p", "s", "q"))]
 
 
 @pytest.fixture
