@@ -192,7 +192,10 @@ struct EpiTag {
 //   mode 0: each XCD gets whole groups of `g` consecutive logical tiles
 //           (tiles that share operands, e.g. the channel tiles of one pixel
 //           block), groups rotating over the XCDs so a heavy-first phase
-//           order stays balanced; a tail that fills no 8 groups is unchanged.
+//           order stays balanced; a tail that fills no 8 groups goes to
+//           the XCDs in contiguous ranges, as in mode 1, so that a group of
+//           the tail shares fewer L2s (two, for 32 tail workgroups in
+//           groups of 8, where round-robin placement gave eight).
 //   mode 1: each XCD gets one contiguous eighth of the logical tiles (tiles
 //           ordered so that neighbours share operands then share an L2).
 __device__ inline int xcd_remap(int b, int total, int g, int mode)
@@ -205,8 +208,12 @@ __device__ inline int xcd_remap(int b, int total, int g, int mode)
     }
     const int span = 8 * g;
     const int main_part = (total / span) * span;
-    if (b >= main_part)
-        return b;
+    if (b >= main_part) {        // main_part is a multiple of 8: b and b - main_part share the XCD
+        const int t = b - main_part, rest = total - main_part;
+        const int xt = t & 7, lt = t >> 3;
+        const int q = rest >> 3, r = rest & 7;
+        return main_part + xt * q + (xt < r ? xt : r) + lt;
+    }
     return ((l / g) * 8 + x) * g + (l % g);
 }
 
