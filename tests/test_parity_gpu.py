@@ -379,6 +379,24 @@ def test_pwide_config_outside_its_layers(shape, epi):
         assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} epi {epi} config {cid}")
 
 
+# Launches of a few rounds of tiles: the grid is trimmed to the fewest
+# workgroups that keep the number of rounds (the persistent GEMM config:
+# 259 tiles on 130 workgroups; the persistent strided config: 546 tiles of
+# four phases on 184), and the workgroups past the last whole span of groups
+# go to the XCDs in contiguous ranges, a tail that is not a multiple of
+# eight. Every config, every element against the oracle.
+@pytest.mark.parametrize("shape", [(337, 14, 14, 128, 64, 1, 1, 1, 0), (67, 30, 31, 200, 64, 3, 3, 1, 1),
+                                   (160, 29, 30, 136, 64, 3, 3, 2, 1)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_trimmed_grids_every_config(shape):
+    cfg = _cfg(shape, EPI_NONE, seed=23)
+    inp = make_inputs(cfg)
+    ref = ref_full(cfg, inp)
+    for cid in range(cb.conv2d_dgrad_num_configs()):
+        note(f"trimmed grid {shape} config {cid} {cb.conv2d_dgrad_config_name(cid)}")
+        assert_close(run(cfg, inp, config_id=cid), ref, f"{shape} config {cid}")
+
+
 # ---------------------------------------------------------------- full sizes
 
 @pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
