@@ -268,7 +268,7 @@ int halo1_private_bytes(int i);
 // of dgrad_halo1.
 int pwide_num_configs();
 const TileConfig& pwide_config(int i);
-bool pwide_admits(int i, int stride, int epi);
+bool pwide_admits(int i, int R, int S, int stride, int epi);
 bool pwide_runs_launch(int i, const KernelArgs& a);   // no zero phases, no split
 hipError_t launch_pwide(int i, const KernelArgs& a, hipStream_t stream);
 int pwide_blocks_per_cu(int i);

@@ -944,7 +944,7 @@ bool tile_config_admits(int id, int R, int S, int stride, int pad, int H, int W,
     case 2: return halo_admits(i, R, S, stride, pad, H, W, P, Q);
     case 3: return pgemm_admits(i, R, S, stride, pad, K, epi);
     case 4: return halo1_admits(i, R, S, stride, pad, H, W, P, Q, K, epi);
-    case 5: return pwide_admits(i, stride, epi);
+    case 5: return pwide_admits(i, R, S, stride, epi);
     default: return true;
     }
 }

@@ -509,8 +509,10 @@ dgrad_pwide(KernelArgs a)
 }
 
 // The layers this kernel runs: stride at least 2 (so several phases share a
-// launch), no fused epilogue factor.
-bool pwide_fits(int stride, int epi) { return stride >= 2 && epi == kEpiNone; }
+// launch), a filter at least as wide and tall as the stride (so every phase
+// has taps: phase p's taps are those r = p + pad mod s, one exists for every
+// p when R >= s), no fused epilogue factor.
+bool pwide_fits(int R, int S, int stride, int epi) { return stride >= 2 && R >= stride && S >= stride && epi == kEpiNone; }
 
 // The launches this kernel runs: GEMM tiles only (no zero phase: those go to
 // dgrad_igemm), no split, the grid no larger than the tiles; the
@@ -518,7 +520,7 @@ bool pwide_fits(int stride, int epi) { return stride >= 2 && epi == kEpiNone; }
 bool pwide_runs(const KernelArgs& a)
 {
     return !a.sk && a.nzphases == 0 && a.zstripes == 0 && a.ncomp == 0 && a.total_tiles == a.gemm_tiles &&
-           pwide_fits(a.stride, a.epi) && a.grid >= 1 && a.grid <= a.gemm_tiles &&
+           pwide_fits(a.R, a.S, a.stride, a.epi) && a.grid >= 1 && a.grid <= a.gemm_tiles &&
            (a.order != 2 || a.grid % a.nphases == 0);
 }
 
@@ -577,7 +579,7 @@ int pwide_num_configs() { return kNumPwide; }
 
 const TileConfig& pwide_config(int i) { return kPwideConfigs[i]; }
 
-bool pwide_admits(int i, int stride, int epi) { return i >= 0 && i < kNumPwide && pwide_fits(stride, epi); }
+bool pwide_admits(int i, int R, int S, int stride, int epi) { return i >= 0 && i < kNumPwide && pwide_fits(R, S, stride, epi); }
 
 bool pwide_runs_launch(int i, const KernelArgs& a) { return i >= 0 && i < kNumPwide && pwide_runs(a); }
 
